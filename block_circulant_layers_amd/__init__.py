@@ -1,0 +1,18 @@
+"""MI355X-native in-place packed real FFT (rdFFT) and block-circulant layers.
+
+The compute path is the HIP library ``lib/librdfft.so`` (C ABI in
+``include/rdfft.h``); :mod:`block_circulant_layers_amd.binding` is its thin
+Python binding.  Build with ``python -m block_circulant_layers_amd.build``.
+"""
+
+from .binding import (  # noqa: F401
+    RDFFT_BF16,
+    RDFFT_F32,
+    RdfftError,
+    circulant_bwd,
+    circulant_fwd,
+    lib,
+    lib_path,
+    rdfft_forward,
+    rdfft_inverse,
+)

@@ -1,0 +1,168 @@
+"""Thin ctypes binding of librdfft.so (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/rdfft.h``; this module only turns torch tensors into device
+pointers, sizes and the current HIP stream, allocates outputs with torch, and
+raises on a nonzero status.  There is no CPU path: tensors must live on a GPU
+and the library must be built (``python -m block_circulant_layers_amd.build``),
+otherwise the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RdfftError",
+    "lib",
+    "lib_path",
+    "rdfft_forward",
+    "rdfft_inverse",
+    "circulant_fwd",
+    "circulant_bwd",
+    "RDFFT_F32",
+    "RDFFT_BF16",
+]
+
+RDFFT_F32 = 0
+RDFFT_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# exported symbol -> (restype, argtypes); mirrors include/rdfft.h
+_I64 = ctypes.c_int64
+_VP = ctypes.c_void_p
+SIGNATURES = {
+    "rdfft_abi_version": (ctypes.c_int, []),
+    "rdfft_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rdfft_forward": (ctypes.c_int, [_VP, _I64, _I64, ctypes.c_int, _VP]),
+    "rdfft_inverse": (ctypes.c_int, [_VP, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_bwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+}
+
+
+class RdfftError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        msg = lib().rdfft_status_string(status).decode()
+        super().__init__(f"{func} failed: status {status} ({msg})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.environ.get("RDFFT_LIB", os.path.join(_HERE, "lib", "librdfft.so"))
+
+
+def lib() -> ctypes.CDLL:
+    """Load librdfft.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} not found: build it with `python -m block_circulant_layers_amd.build` "
+                "(there is no fallback implementation)"
+            )
+        cdll = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(cdll, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = cdll
+    return _LIB
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RDFFT_F32
+    if t.dtype == torch.bfloat16:
+        return RDFFT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _check_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise RdfftError(name, st)
+
+
+def rdfft_forward(data: torch.Tensor, stream=None) -> torch.Tensor:
+    """In-place packed forward transform of the rows (last axis) of ``data``."""
+    _check_gpu(data)
+    p = data.shape[-1] if data.dim() else 0
+    rows = data.numel() // p if p else 0
+    _call("rdfft_forward", data.data_ptr(), rows, p, _dtype_code(data), _stream(data, stream))
+    return data
+
+
+def rdfft_inverse(data: torch.Tensor, stream=None) -> torch.Tensor:
+    """In-place inverse of :func:`rdfft_forward` (carries 1/p)."""
+    _check_gpu(data)
+    p = data.shape[-1] if data.dim() else 0
+    rows = data.numel() // p if p else 0
+    _call("rdfft_inverse", data.data_ptr(), rows, p, _dtype_code(data), _stream(data, stream))
+    return data
+
+
+def _circ_dims(x: torch.Tensor, c: torch.Tensor):
+    if c.dim() != 3 or c.dtype != torch.float32:
+        raise ValueError("c must be a float32 tensor of shape (q, k, p)")
+    q, k, p = c.shape
+    if x.shape[-1] != k * p:
+        raise ValueError(f"x has {x.shape[-1]} features, c implies d_in = {k * p}")
+    batch = x.numel() // x.shape[-1]
+    return q, k, p, batch
+
+
+def circulant_fwd(x: torch.Tensor, c: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = block-circulant(c) applied to every row of x; returns y (allocated if None)."""
+    q, k, p, batch = _circ_dims(x, c)
+    if y is None:
+        y = torch.empty(*x.shape[:-1], q * p, dtype=x.dtype, device=x.device)
+    _check_gpu(x, c, y)
+    if y.dtype != x.dtype:
+        raise ValueError("y must have the dtype of x")
+    _call("circulant_fwd", x.data_ptr(), c.data_ptr(), y.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
+          _stream(x, stream))
+    return y
+
+
+def circulant_bwd(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor | None = None,
+                  dc: torch.Tensor | None = None, need_dx: bool = True, need_dc: bool = True, stream=None):
+    """Returns (dx, dc) for upstream gradient dy; dc is overwritten, not accumulated."""
+    q, k, p, batch = _circ_dims(x, c)
+    if need_dx and dx is None:
+        dx = torch.empty_like(x)
+    if need_dc and dc is None:
+        dc = torch.empty_like(c)
+    _check_gpu(x, c, dy, dx, dc)
+    if dy.dtype != x.dtype or (dx is not None and dx.dtype != x.dtype):
+        raise ValueError("dy and dx must have the dtype of x")
+    if dy.numel() != batch * q * p:
+        raise ValueError("dy must have shape (..., d_out)")
+    _call("circulant_bwd", x.data_ptr(), c.data_ptr(), dy.data_ptr(),
+          dx.data_ptr() if dx is not None else None, dc.data_ptr() if dc is not None else None,
+          batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
+    return dx, dc

@@ -1,0 +1,439 @@
+// rdfft_device.hpp -- gfx950 device building blocks of the in-place packed real FFT.
+//
+// Method: "Memory-Efficient Training with In-Place FFT Implementation"
+// (Paper-Notes page, sections "Squeeze", "四元素对称群 (Proposition 1)",
+// "原地 IFFT 设计").
+//
+// Packed layout of an r-point spectrum (r a power of two): slot 0 = y_0,
+// slot r/2 = y_{r/2}, slot k = Re y_k, slot r-k = Im y_k (0 < k < r/2).
+//
+// Forward = radix-2 decimation in time on bit-reversed input.  Stage m merges,
+// inside each m-block at g, the packed m/2-point spectra E (first half) and O
+// (second half) in place:
+//   DC pair      (g, g+m/2)                   (E0, O0) -> (E0+O0, E0-O0)
+//   quarter pair (g+m/4, g+3m/4), m >= 4      slot g+3m/4 negated
+//   group        {g+k, g+m/2-k, g+m/2+k, g+m-k}, 0 < k < m/4:
+//                (ReE, ImE, ReO, ImO) -> (Re(E+t), Re(E-t), -Im(E-t), Im(E+t)),
+//                t = W_m^k O, W_m = exp(-2 pi i / m)
+// The inverse runs the same graph backwards; every inverse group returns
+// (2E, 2O), so all per-stage halvings are applied once at the end as 1/r.
+//
+// GPU organisation (ours, not the pages'): a row of P reals is owned by
+// T = P/E threads holding E values each.  Stages are grouped into passes.
+//   * pass 0: thread t loads x[t + T*s] (s < E: coalesced across threads) and
+//     runs stages 2..E in registers: the packed E-point spectrum of the
+//     decimated subsequence with residue t mod T.
+//   * pass with input spectra of size B and radix R (output size B*R): the
+//     packed slots congruent to +-k mod B of the R sub-spectra that merge form
+//     a set closed under stages 2B..B*R, so an "item" (output residue r',
+//     class k) runs those log2(R) stages in registers.  Class k = 0 holds the
+//     slots 0 and B/2 of each sub-spectrum (an R-point real transform plus a
+//     half-bin-shifted one, all with constant twiddles).
+//   * between passes the row goes through LDS in a padded residue-major layout
+//     A(r, s) = r*(B+1) + s (the +1 keeps row-strided accesses off one bank).
+//   * the last pass stores the natural packed layout directly (coalesced).
+// Twiddles: one table load per stage per item (W_m^k), the others of the item
+// derived by multiplication with compile-time constants; the constants fold.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rdfft {
+
+struct Tw {
+  float c, s;  // W = c - i s   (c = cos(theta), s = sin(theta), W = exp(-i theta))
+};
+
+#include "twiddles.inc"
+
+// ---------------------------------------------------------------------------
+// compile-time helpers
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
+__host__ __device__ constexpr int bitrev(int v, int bits) {
+  int r = 0;
+  for (int i = 0; i < bits; ++i)
+    if ((v >> i) & 1) r |= 1 << (bits - 1 - i);
+  return r;
+}
+__host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Twiddle of angle 2 pi * num / den, 0 <= num/den <= 1/4, from the table.
+__device__ __forceinline__ Tw tw_const(int num, int den) { return kTw[num * (kTwN / den)]; }
+
+// angle(w) + alpha, alpha = 2 pi num / den constant in [0, pi/2]
+__device__ __forceinline__ Tw tw_add(Tw w, int num, int den) {
+  if (num == 0) return w;
+  if (4 * num == den) return Tw{-w.s, w.c};
+  const Tw a = tw_const(num, den);
+  return Tw{a.c * w.c - a.s * w.s, a.c * w.s + a.s * w.c};
+}
+// alpha - angle(w), alpha = 2 pi num / den constant in (0, pi/2]
+__device__ __forceinline__ Tw tw_sub_from(int num, int den, Tw w) {
+  if (4 * num == den) return Tw{w.s, w.c};
+  const Tw a = tw_const(num, den);
+  return Tw{a.c * w.c + a.s * w.s, a.s * w.c - a.c * w.s};
+}
+
+// ---------------------------------------------------------------------------
+// the pages' in-place operations on one four-element group
+// slots (g+k, g+m/2-k, g+m/2+k, g+m-k) = (a1, a2, a3, a4)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void grp_fwd(float& a1, float& a2, float& a3, float& a4, Tw w) {
+  // in: (Re E, Im E, Re O, Im O);  t = W O with W = c - i s
+  const float tr = w.c * a3 + w.s * a4;
+  const float ti = w.c * a4 - w.s * a3;
+  const float er = a1, ei = a2;
+  a1 = er + tr;  // Re y_k
+  a2 = er - tr;  // Re y_{m/2-k} = Re(E - t)
+  a3 = ti - ei;  // Im y_{m/2-k} = -Im(E - t)
+  a4 = ei + ti;  // Im y_k
+}
+
+__device__ __forceinline__ void grp_inv(float& a1, float& a2, float& a3, float& a4, Tw w) {
+  // in: (Re y_k, Re y_{m/2-k}, Im y_{m/2-k}, Im y_k);  y_{m/2+k} = conj(y_{m/2-k})
+  // out: (Re 2E, Im 2E, Re 2O, Im 2O),  2E = y_k + y_{m/2+k},  2O = (y_k - y_{m/2+k}) conj(W)
+  const float er = a1 + a2, ei = a4 - a3;
+  const float tr = a1 - a2, ti = a4 + a3;
+  a1 = er;
+  a2 = ei;
+  a3 = tr * w.c - ti * w.s;
+  a4 = tr * w.s + ti * w.c;
+}
+
+// ---------------------------------------------------------------------------
+// complete packed R-point transform in registers on a[S*q], q < R, input in
+// bit-reversed order (forward) / natural packed (inverse)
+// ---------------------------------------------------------------------------
+template <int R, int S>
+__device__ __forceinline__ void small_fwd(float* a) {
+#pragma unroll
+  for (int m = 2; m <= R; m *= 2) {
+#pragma unroll
+    for (int g = 0; g < R; g += m) {
+      const float e0 = a[S * g], o0 = a[S * (g + m / 2)];
+      a[S * g] = e0 + o0;
+      a[S * (g + m / 2)] = e0 - o0;
+      if (m >= 4) a[S * (g + 3 * m / 4)] = -a[S * (g + 3 * m / 4)];
+#pragma unroll
+      for (int k = 1; k < m / 4; ++k)
+        grp_fwd(a[S * (g + k)], a[S * (g + m / 2 - k)], a[S * (g + m / 2 + k)], a[S * (g + m - k)],
+                tw_const(k, m));
+    }
+  }
+}
+
+template <int R, int S>
+__device__ __forceinline__ void small_inv(float* a) {
+#pragma unroll
+  for (int m = R; m >= 2; m /= 2) {
+#pragma unroll
+    for (int g = 0; g < R; g += m) {
+#pragma unroll
+      for (int k = 1; k < m / 4; ++k)
+        grp_inv(a[S * (g + k)], a[S * (g + m / 2 - k)], a[S * (g + m / 2 + k)], a[S * (g + m - k)],
+                tw_const(k, m));
+      if (m >= 4) {
+        a[S * (g + m / 4)] = 2.0f * a[S * (g + m / 4)];
+        a[S * (g + 3 * m / 4)] = -2.0f * a[S * (g + 3 * m / 4)];
+      }
+      const float y0 = a[S * g], yh = a[S * (g + m / 2)];
+      a[S * g] = y0 + yh;
+      a[S * (g + m / 2)] = y0 - yh;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// item of a pass (input spectra of size B, radix R), class 0 < k < B/2.
+// a[2q] = slot qB + k, a[2q+1] = slot qB + B - k of the (B*R)-block, q < R.
+// Stage s (m = 2B 2^s) holds, per m-block (q in [base, base + 2^(s+1))),
+// the groups kappa = k + B i and kappa = B(i+1) - k, i < 2^(s-1)
+// (only kappa = k when s = 0).
+// ---------------------------------------------------------------------------
+template <int B, int R, bool INV>
+__device__ __forceinline__ void item_stage(float* a, int s, Tw w) {
+  const int nblk = R >> (s + 1);
+#pragma unroll
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int base = blk << (s + 1);
+    const int h = 1 << s;
+    if (s == 0) {
+      if (INV)
+        grp_inv(a[2 * base], a[2 * base + 1], a[2 * base + 2], a[2 * base + 3], w);
+      else
+        grp_fwd(a[2 * base], a[2 * base + 1], a[2 * base + 2], a[2 * base + 3], w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < h / 2; ++i) {
+        const Tw wa = tw_add(w, i, 2 * h);            // W_m^(k + B i)
+        const Tw wb = tw_sub_from(i + 1, 2 * h, w);   // W_m^(B(i+1) - k)
+        float& f1 = a[2 * (base + i)];
+        float& m1 = a[2 * (base + i) + 1];
+        float& f2 = a[2 * (base + h - i - 1)];
+        float& m2 = a[2 * (base + h - i - 1) + 1];
+        float& f3 = a[2 * (base + h + i)];
+        float& m3 = a[2 * (base + h + i) + 1];
+        float& f4 = a[2 * (base + 2 * h - i - 1)];
+        float& m4 = a[2 * (base + 2 * h - i - 1) + 1];
+        if (INV) {
+          grp_inv(f1, m2, f3, m4, wa);
+          grp_inv(m1, f2, m3, f4, wb);
+        } else {
+          grp_fwd(f1, m2, f3, m4, wa);
+          grp_fwd(m1, f2, m3, f4, wb);
+        }
+      }
+    }
+  }
+}
+
+template <int B, int R>
+__device__ __forceinline__ void item_fwd(float* a, int k) {
+  constexpr int NS = ilog2(R);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int lm = ilog2(2 * B) + s;  // log2 of the stage size m
+    const Tw w = kTw[k << (12 - lm)];  // W_m^k, k/m < 1/4
+    item_stage<B, R, false>(a, s, w);
+  }
+}
+
+template <int B, int R>
+__device__ __forceinline__ void item_inv(float* a, int k) {
+  constexpr int NS = ilog2(R);
+#pragma unroll
+  for (int s = NS - 1; s >= 0; --s) {
+    const int lm = ilog2(2 * B) + s;
+    const Tw w = kTw[k << (12 - lm)];
+    item_stage<B, R, true>(a, s, w);
+  }
+}
+
+// class k = 0: a[2q] = slot qB (an R-point real transform, constant twiddles),
+// a[2q+1] = slot qB + B/2 (half-bin shifted: groups kappa = B/2 + cB with
+// W_m^kappa = W_(2^(s+2))^(2c+1); at s = 0 only the quarter-pair negation).
+template <int R, bool INV>
+__device__ __forceinline__ void item0_odd_stage(float* a, int s) {
+  const int nblk = R >> (s + 1);
+#pragma unroll
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int base = blk << (s + 1);
+    const int h = 1 << s;
+    if (s == 0) {
+      // quarter pair of stage 2B: slot g + 3B/2 = a[2(base+1)+1]
+      if (INV) {
+        a[2 * base + 1] = 2.0f * a[2 * base + 1];
+        a[2 * base + 3] = -2.0f * a[2 * base + 3];
+      } else {
+        a[2 * base + 3] = -a[2 * base + 3];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < h / 2; ++c) {
+        const Tw w = tw_const(2 * c + 1, 4 * h);
+        float& a1 = a[2 * (base + c) + 1];
+        float& a2 = a[2 * (base + h - c - 1) + 1];
+        float& a3 = a[2 * (base + h + c) + 1];
+        float& a4 = a[2 * (base + 2 * h - c - 1) + 1];
+        if (INV)
+          grp_inv(a1, a2, a3, a4, w);
+        else
+          grp_fwd(a1, a2, a3, a4, w);
+      }
+    }
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void item0_fwd(float* a) {
+  small_fwd<R, 2>(a);
+#pragma unroll
+  for (int s = 0; s < ilog2(R); ++s) item0_odd_stage<R, false>(a, s);
+}
+
+template <int R>
+__device__ __forceinline__ void item0_inv(float* a) {
+#pragma unroll
+  for (int s = ilog2(R) - 1; s >= 0; --s) item0_odd_stage<R, true>(a, s);
+  small_inv<R, 2>(a);
+}
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+struct F32Io {
+  using T = float;
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+struct Bf16Io {
+  using T = uint16_t;
+  static __device__ __forceinline__ float load(const uint16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, float v) {
+    *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+  }
+};
+
+// ---------------------------------------------------------------------------
+// one row of P reals, T = P/E threads (t = thread index within the row)
+// ---------------------------------------------------------------------------
+template <int P, int E>
+struct Row {
+  static_assert((P & (P - 1)) == 0 && P >= 2 && P <= 4096, "P must be a power of two in [2, 4096]");
+  static_assert(E <= P && (E & (E - 1)) == 0 && E >= 2, "E must be a power of two <= P");
+  static constexpr int T = P / E;
+  static constexpr int LDS = P + T;  // floats of LDS a row needs (largest padded layout)
+
+  // layout of an exchange whose spectra have size B: residue r, slot s
+  template <int B>
+  static __device__ __forceinline__ int addr(int r, int s) { return r * (B + 1) + s; }
+
+  // pass descriptors, input size B
+  template <int B>
+  struct Pass {
+    static constexpr int R = cmin(P / B, E / 2);
+    static constexpr int BP = B * R;
+    static constexpr int NRES = P / BP;
+    static constexpr int IPT = E / (2 * R);
+  };
+
+  // ---- forward ----------------------------------------------------------
+  // pass 0: ld(i) returns x[i]; thread t reads i = t + T*s (coalesced across threads)
+  template <class Ld>
+  static __device__ __forceinline__ void fwd_pass0(float (&a)[E], Ld ld, int t) {
+    constexpr int LE = ilog2(E);
+#pragma unroll
+    for (int s = 0; s < E; ++s) a[bitrev(s, LE)] = ld(t + T * s);
+    small_fwd<E, 1>(a);
+  }
+
+  static __device__ __forceinline__ void fwd_pass0_scatter(const float (&a)[E], float* L, int t) {
+#pragma unroll
+    for (int s = 0; s < E; ++s) L[addr<E>(t, s)] = a[s];
+  }
+
+  // gather items of the pass with input size B from LDS (layout B) and run it
+  template <int B>
+  static __device__ __forceinline__ void fwd_pass(float (&a)[E], const float* L, int t) {
+    using PS = Pass<B>;
+    constexpr int R = PS::R, LR = ilog2(R);
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int it = t + T * n;
+      const int rp = it % PS::NRES, k = it / PS::NRES;
+      const int k2 = (k == 0) ? (B / 2) : (B - k);
+      float* v = a + 2 * R * n;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const int r = rp + PS::NRES * bitrev(q, LR);
+        v[2 * q] = L[addr<B>(r, k)];
+        v[2 * q + 1] = L[addr<B>(r, k2)];
+      }
+      if (k == 0)
+        item0_fwd<R>(v);
+      else
+        item_fwd<B, R>(v, k);
+    }
+  }
+
+  // write the items of pass B to LDS in layout B*R
+  template <int B>
+  static __device__ __forceinline__ void pass_scatter(const float (&a)[E], float* L, int t) {
+    using PS = Pass<B>;
+    constexpr int R = PS::R;
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int it = t + T * n;
+      const int rp = it % PS::NRES, k = it / PS::NRES;
+      const int k2 = (k == 0) ? (B / 2) : (B - k);
+      const float* v = a + 2 * R * n;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        L[addr<PS::BP>(rp, q * B + k)] = v[2 * q];
+        L[addr<PS::BP>(rp, q * B + k2)] = v[2 * q + 1];
+      }
+    }
+  }
+
+  // store the items of the last pass (B*R == P) in natural packed order: st(slot, value)
+  template <int B, class St>
+  static __device__ __forceinline__ void last_store(const float (&a)[E], int t, St st) {
+    using PS = Pass<B>;
+    static_assert(PS::BP == P, "not the last pass");
+    constexpr int R = PS::R;
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int k = t + T * n;
+      const int k2 = (k == 0) ? (B / 2) : (B - k);
+      const float* v = a + 2 * R * n;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        st(q * B + k, v[2 * q]);
+        st(q * B + k2, v[2 * q + 1]);
+      }
+    }
+  }
+
+  // ---- inverse -----------------------------------------------------------
+  // gather items of inverse pass B (input spectra of size B*R) from `src`
+  // (LDS in layout B*R, or global natural packed when B*R == P) and run it
+  template <int B, class Src>
+  static __device__ __forceinline__ void inv_pass(float (&a)[E], Src src, int t) {
+    using PS = Pass<B>;
+    constexpr int R = PS::R;
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int it = t + T * n;
+      const int rp = it % PS::NRES, k = it / PS::NRES;
+      const int k2 = (k == 0) ? (B / 2) : (B - k);
+      float* v = a + 2 * R * n;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        v[2 * q] = src(addr<PS::BP>(rp, q * B + k));
+        v[2 * q + 1] = src(addr<PS::BP>(rp, q * B + k2));
+      }
+      if (k == 0)
+        item0_inv<R>(v);
+      else
+        item_inv<B, R>(v, k);
+    }
+  }
+
+  // write the items of inverse pass B to LDS in layout B
+  template <int B>
+  static __device__ __forceinline__ void inv_scatter(const float (&a)[E], float* L, int t) {
+    using PS = Pass<B>;
+    constexpr int R = PS::R, LR = ilog2(R);
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int it = t + T * n;
+      const int rp = it % PS::NRES, k = it / PS::NRES;
+      const int k2 = (k == 0) ? (B / 2) : (B - k);
+      const float* v = a + 2 * R * n;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const int r = rp + PS::NRES * bitrev(q, LR);
+        L[addr<B>(r, k)] = v[2 * q];
+        L[addr<B>(r, k2)] = v[2 * q + 1];
+      }
+    }
+  }
+
+  // inverse pass 0: gather residue t's E-point spectrum from LDS (layout E),
+  // invert, store x[t + T s] = value * scale through st(i, v)
+  template <class St>
+  static __device__ __forceinline__ void inv_pass0_store(float (&a)[E], const float* L, int t, float scale, St st) {
+    constexpr int LE = ilog2(E);
+#pragma unroll
+    for (int s = 0; s < E; ++s) a[s] = L[addr<E>(t, s)];
+    small_inv<E, 1>(a);
+#pragma unroll
+    for (int s = 0; s < E; ++s) st(t + T * s, a[bitrev(s, LE)] * scale);
+  }
+};
+
+}  // namespace rdfft

@@ -1,0 +1,201 @@
+// rdfft_lib.hip -- C ABI of librdfft.so: argument checks, kernel selection, launches.
+#include <hip/hip_runtime.h>
+
+#include "rdfft.h"
+#include "rdfft_kernels.hpp"
+#include "circulant_kernels.hpp"
+#include "rdfft_validate.hpp"
+
+namespace rdfft {
+namespace {
+
+int launch_status() { return hipGetLastError() == hipSuccess ? RDFFT_OK : RDFFT_ERR_LAUNCH; }
+
+template <int P, class Io, bool INV>
+int launch_rdfft(void* data, int64_t rows, hipStream_t stream) {
+  constexpr int E = elems_per_thread(P);
+  constexpr int NT = wg_threads(P, E);
+  constexpr int ROWS = NT / (P / E);
+  const int64_t grid = (rows + ROWS - 1) / ROWS;
+  if (grid > 0x7fffffff) return RDFFT_ERR_SIZE;
+  auto* d = static_cast<typename Io::T*>(data);
+  if (INV)
+    rdfft_inv_kernel<P, Io><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(d, rows);
+  else
+    rdfft_fwd_kernel<P, Io><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(d, rows);
+  return launch_status();
+}
+
+template <class Io, bool INV>
+int dispatch_rdfft(void* data, int64_t rows, int64_t p, hipStream_t s) {
+  switch (p) {
+    case 2: return launch_rdfft<2, Io, INV>(data, rows, s);
+    case 4: return launch_rdfft<4, Io, INV>(data, rows, s);
+    case 8: return launch_rdfft<8, Io, INV>(data, rows, s);
+    case 16: return launch_rdfft<16, Io, INV>(data, rows, s);
+    case 32: return launch_rdfft<32, Io, INV>(data, rows, s);
+    case 64: return launch_rdfft<64, Io, INV>(data, rows, s);
+    case 128: return launch_rdfft<128, Io, INV>(data, rows, s);
+    case 256: return launch_rdfft<256, Io, INV>(data, rows, s);
+    case 512: return launch_rdfft<512, Io, INV>(data, rows, s);
+    case 1024: return launch_rdfft<1024, Io, INV>(data, rows, s);
+    case 2048: return launch_rdfft<2048, Io, INV>(data, rows, s);
+    case 4096: return launch_rdfft<4096, Io, INV>(data, rows, s);
+    default: return RDFFT_ERR_SIZE;
+  }
+}
+
+// ---- block-circulant layer -------------------------------------------------
+
+constexpr int kDcTargetWgs = 256;  // aim of the dc token split (workgroups in flight)
+
+template <int P, class Io>
+int launch_circ_mm(const void* in, const float* c, void* out, int64_t batch, int64_t nin, int64_t nout, bool trans,
+                   hipStream_t s) {
+  constexpr MmParams K = mm_params(P);
+  const int64_t gx = (batch + K.tb - 1) / K.tb, gy = (nout + K.to - 1) / K.to;
+  if (gx > 0x7fffffff || gy > 65535 || nin > 0x7fffffff || nout > 0x7fffffff) return RDFFT_ERR_SIZE;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+  const auto* pi = static_cast<const typename Io::T*>(in);
+  auto* po = static_cast<typename Io::T*>(out);
+  if (trans)
+    circ_mm_kernel<P, true, Io><<<grid, dim3(K.nt), 0, s>>>(pi, c, po, batch, int(nin), int(nout));
+  else
+    circ_mm_kernel<P, false, Io><<<grid, dim3(K.nt), 0, s>>>(pi, c, po, batch, int(nin), int(nout));
+  return launch_status();
+}
+
+int launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  fill_zero_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(p, n);
+  return launch_status();
+}
+
+template <int P, class Io>
+int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s) {
+  constexpr DcParams K = dc_params(P);
+  const int64_t gy = (q + K.ti - 1) / K.ti, gz = (k + K.tj - 1) / K.tj;
+  if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
+  int64_t want_x = kDcTargetWgs / (gy * gz);
+  if (want_x < 1) want_x = 1;
+  int64_t tpw = (batch + want_x - 1) / want_x;
+  tpw = (tpw + K.tb - 1) / K.tb * K.tb;
+  const int64_t gx = (batch + tpw - 1) / tpw;
+  if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
+  int st = launch_fill_zero(dc, q * k * P, s);
+  if (st != RDFFT_OK) return st;
+  circ_dc_kernel<P, Io><<<dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(K.nt), 0, s>>>(
+      static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k), int(q), tpw);
+  st = launch_status();
+  if (st != RDFFT_OK) return st;
+  return launch_rdfft<P, F32Io, true>(dc, q * k, s);
+}
+
+template <int P, class Io>
+int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, hipStream_t s) {
+  return launch_circ_mm<P, Io>(x, c, y, batch, d_in / P, d_out / P, false, s);
+}
+
+template <int P, class Io>
+int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
+               int64_t d_out, hipStream_t s) {
+  const int64_t k = d_in / P, q = d_out / P;
+  if (batch == 0) return dc ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
+  if (dx) {
+    const int st = launch_circ_mm<P, Io>(dy, c, dx, batch, q, k, true, s);
+    if (st != RDFFT_OK) return st;
+  }
+  if (dc) return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s);
+  return RDFFT_OK;
+}
+
+#define RDFFT_P_SWITCH(p, CALL)      \
+  switch (p) {                       \
+    case 2: return CALL(2);          \
+    case 4: return CALL(4);          \
+    case 8: return CALL(8);          \
+    case 16: return CALL(16);        \
+    case 32: return CALL(32);        \
+    case 64: return CALL(64);        \
+    case 128: return CALL(128);      \
+    case 256: return CALL(256);      \
+    case 512: return CALL(512);      \
+    case 1024: return CALL(1024);    \
+    case 2048: return CALL(2048);    \
+    case 4096: return CALL(4096);    \
+    default: return RDFFT_ERR_SIZE;  \
+  }
+
+template <class Io>
+int circ_fwd_dispatch(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, int64_t p,
+                      hipStream_t s) {
+#define CALL(P) circ_fwd_p<P, Io>(x, c, y, batch, d_in, d_out, s)
+  RDFFT_P_SWITCH(p, CALL)
+#undef CALL
+}
+
+template <class Io>
+int circ_bwd_dispatch(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
+                      int64_t d_out, int64_t p, hipStream_t s) {
+#define CALL(P) circ_bwd_p<P, Io>(x, c, dy, dx, dc, batch, d_in, d_out, s)
+  RDFFT_P_SWITCH(p, CALL)
+#undef CALL
+}
+
+template <bool INV>
+int rdfft_entry(void* data, int64_t rows, int64_t p, int dtype, void* stream) {
+  const int st = check_rdfft(data, rows, p, dtype);
+  if (st != RDFFT_OK || rows == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == RDFFT_BF16 ? dispatch_rdfft<Bf16Io, INV>(data, rows, p, s)
+                             : dispatch_rdfft<F32Io, INV>(data, rows, p, s);
+}
+
+}  // namespace
+}  // namespace rdfft
+
+extern "C" {
+
+int rdfft_abi_version(void) { return RDFFT_ABI_VERSION; }
+
+const char* rdfft_status_string(int status) {
+  switch (status) {
+    case RDFFT_OK: return "ok";
+    case RDFFT_ERR_NULL: return "null pointer";
+    case RDFFT_ERR_SIZE: return "unsupported size (p must be a power of two in [2, 4096]; counts >= 0)";
+    case RDFFT_ERR_SHAPE: return "d_in and d_out must be positive multiples of p";
+    case RDFFT_ERR_DTYPE: return "unknown dtype";
+    case RDFFT_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RDFFT_ERR_ALIAS: return "output buffer overlaps another buffer";
+    case RDFFT_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int rdfft_forward(void* data, int64_t rows, int64_t p, int dtype, void* stream) {
+  return rdfft::rdfft_entry<false>(data, rows, p, dtype, stream);
+}
+
+int rdfft_inverse(void* data, int64_t rows, int64_t p, int dtype, void* stream) {
+  return rdfft::rdfft_entry<true>(data, rows, p, dtype, stream);
+}
+
+int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, int64_t p,
+                  int dtype, void* stream) {
+  const int st = rdfft::check_circulant_fwd(x, c, y, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK || batch == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == RDFFT_BF16 ? rdfft::circ_fwd_dispatch<rdfft::Bf16Io>(x, c, y, batch, d_in, d_out, p, s)
+                             : rdfft::circ_fwd_dispatch<rdfft::F32Io>(x, c, y, batch, d_in, d_out, p, s);
+}
+
+int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
+                  int64_t d_out, int64_t p, int dtype, void* stream) {
+  const int st = rdfft::check_circulant_bwd(x, c, dy, dx, dc, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == RDFFT_BF16 ? rdfft::circ_bwd_dispatch<rdfft::Bf16Io>(x, c, dy, dx, dc, batch, d_in, d_out, p, s)
+                             : rdfft::circ_bwd_dispatch<rdfft::F32Io>(x, c, dy, dx, dc, batch, d_in, d_out, p, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// rdfft_validate.hpp -- host-side argument checks of the C ABI (no HIP calls).
+//
+// Every entry point runs these before enqueuing anything; on failure it
+// returns the status and touches no device memory.
+#pragma once
+
+#include <stdint.h>
+
+#include "rdfft.h"
+
+namespace rdfft {
+
+inline bool valid_len(int64_t p) { return p >= 2 && p <= 4096 && (p & (p - 1)) == 0; }
+inline bool valid_dtype(int dtype) { return dtype == RDFFT_F32 || dtype == RDFFT_BF16; }
+inline int64_t dtype_bytes(int dtype) { return dtype == RDFFT_BF16 ? 2 : 4; }
+inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// half-open byte ranges [a, a+na) and [b, b+nb) overlap
+inline bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + static_cast<uintptr_t>(nb) && pb < pa + static_cast<uintptr_t>(na);
+}
+
+// largest element count any call accepts (keeps every byte offset in int64)
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+inline int check_rdfft(const void* data, int64_t rows, int64_t p, int dtype) {
+  if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;
+  if (!valid_len(p) || rows < 0 || rows > kMaxElems / p) return RDFFT_ERR_SIZE;
+  if (rows == 0) return RDFFT_OK;
+  if (data == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(data)) return RDFFT_ERR_ALIGN;
+  return RDFFT_OK;
+}
+
+inline int check_circulant_dims(int64_t batch, int64_t d_in, int64_t d_out, int64_t p) {
+  if (!valid_len(p) || batch < 0) return RDFFT_ERR_SIZE;
+  if (d_in <= 0 || d_out <= 0 || d_in % p != 0 || d_out % p != 0) return RDFFT_ERR_SHAPE;
+  if (d_in > kMaxElems || d_out > kMaxElems || batch > kMaxElems / d_in || batch > kMaxElems / d_out ||
+      (d_in / p) > kMaxElems / d_out)
+    return RDFFT_ERR_SIZE;
+  return RDFFT_OK;
+}
+
+inline int check_circulant_fwd(const void* x, const float* c, const void* y, int64_t batch, int64_t d_in,
+                               int64_t d_out, int64_t p, int dtype) {
+  if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;
+  const int st = check_circulant_dims(batch, d_in, d_out, p);
+  if (st != RDFFT_OK || batch == 0) return st;
+  if (x == nullptr || c == nullptr || y == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(c) || !aligned16(y)) return RDFFT_ERR_ALIGN;
+  const int64_t eb = dtype_bytes(dtype);
+  const int64_t cbytes = (d_out / p) * d_in * 4;
+  if (overlaps(y, batch * d_out * eb, x, batch * d_in * eb) || overlaps(y, batch * d_out * eb, c, cbytes))
+    return RDFFT_ERR_ALIAS;
+  return RDFFT_OK;
+}
+
+inline int check_circulant_bwd(const void* x, const float* c, const void* dy, const void* dx, const float* dc,
+                               int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype) {
+  if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;
+  const int st = check_circulant_dims(batch, d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  if (dx == nullptr && dc == nullptr) return RDFFT_ERR_NULL;
+  if (batch == 0) {
+    if (dc != nullptr && !aligned16(dc)) return RDFFT_ERR_ALIGN;
+    return RDFFT_OK;
+  }
+  if (x == nullptr || c == nullptr || dy == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(c) || !aligned16(dy) || (dx && !aligned16(dx)) || (dc && !aligned16(dc)))
+    return RDFFT_ERR_ALIGN;
+  const int64_t eb = dtype_bytes(dtype);
+  const int64_t xb = batch * d_in * eb, yb = batch * d_out * eb, cb = (d_out / p) * d_in * 4;
+  if (dx && (overlaps(dx, xb, x, xb) || overlaps(dx, xb, c, cb) || overlaps(dx, xb, dy, yb) ||
+             overlaps(dx, xb, dc, cb)))
+    return RDFFT_ERR_ALIAS;
+  if (dc && (overlaps(dc, cb, x, xb) || overlaps(dc, cb, c, cb) || overlaps(dc, cb, dy, yb)))
+    return RDFFT_ERR_ALIAS;
+  return RDFFT_OK;
+}
+
+}  // namespace rdfft

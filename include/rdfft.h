@@ -1,0 +1,124 @@
+/*
+ * rdfft.h -- C ABI of the MI355X (gfx950) in-place real FFT and block-circulant
+ * layer library (librdfft.so).
+ *
+ * Method: "Memory-Efficient Training with In-Place FFT Implementation"
+ * (NeurIPS 2025, arXiv 2511.01385), as described on the Paper-Notes page
+ * (zhaoyang97.github.io, section "方法详解") and the scime.ai summary page
+ * (sections "Problem" and "Approach").
+ *
+ * Packed layout (Paper-Notes page, "Squeeze"): a real row x of length p (a
+ * power of two) is replaced, in its own p-element buffer, by its DFT
+ * y_k = sum_n x_n exp(-2 pi i k n / p) written as
+ *     [0] = y_0,  [p/2] = y_{p/2},  [k] = Re y_k,  [p-k] = Im y_k  (0 < k < p/2).
+ * y_0 and y_{p/2} are real and y_{p-k} = conj(y_k), so this is lossless.
+ *
+ * Common rules for every entry point
+ *   - Pointers are DEVICE pointers owned by the caller: contiguous, row-major,
+ *     16-byte aligned.  The library allocates no device memory, keeps no
+ *     per-call state and is reentrant.  Its only device data is a read-only
+ *     twiddle table compiled into the code object.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work and return; results are ready when the stream reaches that point.
+ *   - Arguments are checked on the host before anything is enqueued.  On any
+ *     error the call returns a nonzero status and neither reads nor writes
+ *     device memory.  Size 0 (rows or batch) is a no-op returning RDFFT_OK;
+ *     pointers are not checked then.
+ *   - `dtype` selects the storage type of the row data (data, x, y, dy, dx):
+ *     RDFFT_F32 (float) or RDFFT_BF16 (bfloat16).  All arithmetic is fp32;
+ *     bf16 results are rounded to nearest even once, on store.  The
+ *     circulant parameters c and their gradient dc are always float.
+ *   - Supported row / block lengths: p = 2, 4, 8, ..., 4096.
+ *   - Non-finite inputs are propagated, not checked.
+ */
+#ifndef RDFFT_H
+#define RDFFT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RDFFT_ABI_VERSION 1
+
+/* storage types */
+#define RDFFT_F32 0
+#define RDFFT_BF16 1
+
+/* status codes */
+#define RDFFT_OK 0
+#define RDFFT_ERR_NULL 1   /* a required pointer is NULL */
+#define RDFFT_ERR_SIZE 2   /* p not a power of two in [2, 4096], or a negative / too large count */
+#define RDFFT_ERR_SHAPE 3  /* d_in or d_out not a positive multiple of p */
+#define RDFFT_ERR_DTYPE 4  /* dtype not RDFFT_F32 / RDFFT_BF16 */
+#define RDFFT_ERR_ALIGN 5  /* a pointer is not 16-byte aligned */
+#define RDFFT_ERR_ALIAS 6  /* an output buffer overlaps another buffer of the call */
+#define RDFFT_ERR_LAUNCH 7 /* the HIP runtime refused a kernel launch */
+
+/* Version of this ABI (RDFFT_ABI_VERSION of the library that was built). */
+int rdfft_abi_version(void);
+
+/* Static string naming a status code ("ok", "null pointer", ...). */
+const char* rdfft_status_string(int status);
+
+/*
+ * rdfft_forward -- in-place packed forward transform of `rows` rows.
+ *   data  [rows, p] of dtype; on return each row holds its packed spectrum
+ *         (layout above; unnormalised).  Decimation-in-time Cooley-Tukey whose
+ *         every stage updates the four-element conjugate-symmetric groups
+ *         {g+k, g+m/2-k, g+m/2+k, g+m-k} in place (Paper-Notes page,
+ *         "四元素对称群 (Proposition 1)").  No buffer besides `data`.
+ */
+int rdfft_forward(void* data, int64_t rows, int64_t p, int dtype, void* stream);
+
+/*
+ * rdfft_inverse -- in-place inverse of rdfft_forward (carries the 1/p factor).
+ *   data  [rows, p] of dtype holding packed spectra; on return the real rows.
+ *   The butterfly graph of the forward run backwards, each group split into
+ *   its symmetric and antisymmetric parts (Paper-Notes page, "原地 IFFT 设计";
+ *   the per-stage 1/2 is applied once as 1/p, which is exact in binary).
+ *   Any p reals are a valid packed spectrum.
+ */
+int rdfft_inverse(void* data, int64_t rows, int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_fwd -- block-circulant layer forward (Paper-Notes page,
+ * "循环矩阵训练适配"): for every token b and output block i,
+ *     y[b, i*p:(i+1)*p] = IFFT( sum_j FFT(c[i, j, :]) * FFT(x[b, j*p:(j+1)*p]) ),
+ * i.e. y = x W^T with W[i*p + a, j*p + t] = c[i, j, (a - t) mod p].
+ *   x   [batch, d_in]   dtype, read only
+ *   c   [q, k, p]       float (q = d_out/p, k = d_in/p), read only, time domain
+ *   y   [batch, d_out]  dtype, written (must not overlap x or c)
+ * Spectra live only on chip; nothing is written besides y.
+ */
+int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out,
+                  int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_bwd -- gradients of the layer above for an upstream gradient dy
+ * (the pages: products of packed spectra stay conjugate-symmetric, gradients
+ * likewise):
+ *     dx[b, j-block] = IFFT( sum_i conj(FFT(c[i, j])) * FFT(dy[b, i-block]) )   (= dy W)
+ *     dc[i, j, :]    = IFFT( sum_b conj(FFT(x[b, j-block])) * FFT(dy[b, i-block]) )
+ *   x   [batch, d_in]   dtype, read only
+ *   c   [q, k, p]       float, read only
+ *   dy  [batch, d_out]  dtype, read only
+ *   dx  [batch, d_in]   dtype, overwritten; may be NULL to skip it
+ *   dc  [q, k, p]       float, OVERWRITTEN (not accumulated) with the sum over
+ *                       all tokens; may be NULL to skip it.  It serves as the
+ *                       accumulator of the token sum in the packed spectral
+ *                       domain and is transformed back in place, so the order
+ *                       of the fp32 token sum is not fixed (results may differ
+ *                       in the last bits from call to call).
+ * dx and dc must not both be NULL, and must not overlap each other or any
+ * input.  When batch == 0, dc is set to zero (if given).
+ */
+int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
+                  int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RDFFT_H */

@@ -1,0 +1,364 @@
+"""Benchmark of the in-place packed real FFT and the block-circulant layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline step: 4096 rows of p = 512, fp32, forward then inverse rdFFT in
+place (one pass of the transform path over one batch).  Each step works on
+the next of NBUF distinct copies (>= 1 GiB in total) so the 256 MB last-level
+cache cannot hold the data between steps; every buffer is resident in HBM
+before the timed region starts.  `value` = algorithmic bytes (every row read
+once and written once, per transform) / wall time of the K steps.
+
+The JSON line also carries
+  roofline      the forward kernel: algorithmic bytes per launch / its mean
+                launch duration (HIP events around every launch in the timed
+                region, on the launch stream), against 8 TB/s HBM;
+  cpu_baseline  the fp64 oracle (numpy, one thread) on a bounded sample of
+                the same workload, in the same unit;
+  extra         the other transform sizes and the block-circulant layer
+                workloads (tokens/s), each against its own roofline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_circulant_layers_amd as bcl  # noqa: E402
+from block_circulant_layers_amd import synthetic as syn  # noqa: E402
+
+METRIC = "rdFFT GB/s + % HBM peak (p=512,4096); circulant fwd+bwd tokens/s"
+HBM_PEAK_GBS = 8000.0
+VALU_FP32_PEAK_TFS = 157.3
+ROTATE_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_circulant_layers_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; traffic figures taken from counters are only
+    reported while the kernels they were measured on are unchanged."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hpp", ".hip")):
+            with open(os.path.join(CSRC, name), "rb") as fh:
+                h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    path = os.path.join(PROFILES, "traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", txt)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"^\|\s*{re.escape(kernel_key)}\s*\|.*?\|\s*([0-9.]+)\s*\|\s*$", txt, re.M)
+    return float(m.group(1)) if m else None
+
+
+class Timer:
+    """Events on the stream the kernels are launched on (torch's current stream)."""
+
+    def __init__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop(self) -> float:
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+# ---------------------------------------------------------------------------
+# packed transform workloads
+# ---------------------------------------------------------------------------
+
+
+def _graph(fn):
+    """Capture fn() (a sequence of library launches) into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0):
+    """Steps of (forward, inverse) in place on one batch, the batch rotating
+    over nbuf distinct copies.  Launches are replayed from two HIP graphs: all
+    nbuf forwards, then all nbuf inverses (each buffer gets forward then
+    inverse, as in a step).  Events around the forward graph give the forward
+    kernel's mean launch duration."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    eb = 4 if dtype == "f32" else 2
+    nbytes = rows * p * eb
+    nbuf = max(2, ROTATE_BYTES // nbytes)
+    base = syn.torch_normal((rows, p), workload, syn.T_X, index, dtype=tdt)
+    bufs = [base.clone() for _ in range(nbuf)]
+    g_fwd = _graph(lambda: [bcl.rdfft_forward(b) for b in bufs])
+    g_inv = _graph(lambda: [bcl.rdfft_inverse(b) for b in bufs])
+    reps_w = max(1, -(-warmup // nbuf))
+    reps = max(1, -(-steps // nbuf))
+    for _ in range(reps_w):
+        g_fwd.replay()
+        g_inv.replay()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    tm = Timer()
+    torch.cuda.synchronize()
+    tm.start()
+    for r in range(reps):
+        ev[r][0].record()
+        g_fwd.replay()
+        ev[r][1].record()
+        g_inv.replay()
+        ev[r][2].record()
+    ms = tm.stop()
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / (reps * nbuf)
+    inv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / (reps * nbuf)
+    # every buffer has been through (reps + reps_w) round trips: still the input
+    drift = float((bufs[0].float() - base.float()).abs().max() / base.float().abs().max())
+    nsteps = reps * nbuf
+    step_bytes = 2 * 2 * nbytes  # forward + inverse, each reads and writes every row once
+    del bufs, g_fwd, g_inv, base
+    torch.cuda.empty_cache()
+    return {
+        "steps": nsteps,
+        "warmup": reps_w * nbuf,
+        "ms_per_step": ms / nsteps,
+        "gbs": step_bytes / (ms / nsteps) / 1e6,
+        "bytes_per_launch": 2 * nbytes,
+        "fwd_ms": fwd_ms,
+        "inv_ms": inv_ms,
+        "nbuf": nbuf,
+        "roundtrip_drift": drift,
+    }
+
+
+def cpu_baseline_rdfft(rows, p, seconds=10.0):
+    """The fp64 oracle, unmodified, on the headline workload until ~`seconds`."""
+    from oracle import rdfft_oracle as ro
+
+    t, ref = syn.cast_like_device(syn.normal((rows, p), syn.WL_RDFFT_512, syn.T_X), "f32")
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        z = ro.rdfft_forward(ref)
+        ro.rdfft_inverse(z)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    step_bytes = 2 * 2 * rows * p * 4
+    return {
+        "value": round(step_bytes * reps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} x (forward + inverse) of the full {rows}x{p} fp32 batch, float64 numpy "
+        f"(pocketfft, single-threaded), {el:.1f} s",
+    }
+
+
+# ---------------------------------------------------------------------------
+# block-circulant layer workloads
+# ---------------------------------------------------------------------------
+
+
+def circ_algorithmic(batch, d, p, eb):
+    """Bytes and flops of one forward + backward at the algorithmic minimum:
+    activations x, y, x, dy, dx once each; c twice, dc once (fp32)."""
+    nbytes = 5 * batch * d * eb + 3 * (d * d // p) * 4
+    lp = int(np.log2(p))
+    flops = 5 * batch * 2.5 * d * lp + 3 * 2.5 * (d * d / p) * lp + 3 * 4 * batch * d * d / p
+    return nbytes, flops
+
+
+def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
+    q = k = d // p
+    xs = [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, i, dtype=torch.bfloat16) for i in range(nrot)]
+    dys = [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, i, dtype=torch.bfloat16) for i in range(nrot)]
+    c = syn.torch_normal((q, k, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0)
+    ys = [torch.empty_like(x) for x in xs]
+    dxs = [torch.empty_like(x) for x in xs]
+    dc = torch.empty_like(c)
+
+    def rot():
+        for j in range(nrot):
+            bcl.circulant_fwd(xs[j], c, ys[j])
+            bcl.circulant_bwd(xs[j], c, dys[j], dx=dxs[j], dc=dc)
+
+    g = _graph(rot)
+    for _ in range(max(1, -(-warmup // nrot))):
+        g.replay()
+    reps = max(1, -(-steps // nrot))
+    tm = Timer()
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(reps):
+        g.replay()
+    ms = tm.stop() / (reps * nrot)
+    nbytes, flops = circ_algorithmic(batch, d, p, 2)
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (VALU_FP32_PEAK_TFS * 1e12)) * 1e3
+    return {
+        "tokens_per_s": round(batch / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 5),
+        "roofline_ms": round(t_roof, 5),
+        "frac_of_roofline": round(t_roof / ms, 4),
+    }
+
+
+def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=1024):
+    q = k = d // p
+    xs = [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_X, a, dtype=torch.bfloat16) for a in range(n_adapters)]
+    dys = [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_DY, a, dtype=torch.bfloat16) for a in range(n_adapters)]
+    cs = [syn.torch_normal((q, k, p), syn.WL_CIRC_ADAPTERS, syn.T_C, a, scale=1 / 64.0) for a in range(n_adapters)]
+    ys = [torch.empty_like(x) for x in xs]
+    dxs = [torch.empty_like(x) for x in xs]
+    dcs = [torch.empty_like(c) for c in cs]
+
+    def step():
+        for a in range(n_adapters):
+            bcl.circulant_fwd(xs[a], cs[a], ys[a])
+        for a in reversed(range(n_adapters)):
+            bcl.circulant_bwd(xs[a], cs[a], dys[a], dx=dxs[a], dc=dcs[a])
+
+    g = _graph(step)
+    for _ in range(warmup):
+        g.replay()
+    tm = Timer()
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(steps):
+        g.replay()
+    ms = tm.stop() / steps
+    nbytes, flops = circ_algorithmic(batch, d, p, 2)
+    nbytes *= n_adapters
+    flops *= n_adapters
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (VALU_FP32_PEAK_TFS * 1e12)) * 1e3
+    return {
+        "tokens_per_s": round(batch / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4),
+        "roofline_ms": round(t_roof, 4),
+        "frac_of_roofline": round(t_roof / ms, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(
+            f"bench.py measures one GPU only (asked for {args.gpus}); the transform rows and the layer's "
+            "tokens shard with no communication but dc's all-reduce, which is not built here.",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    bcl.lib()
+    if args.calib_copy:
+        a = torch.ones(64 << 20, device="cuda:0")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    rows, p = 4096, 512
+    log(f"headline: rdfft {rows}x{p} f32 fwd+inv, warmup {args.warmup}, steps {args.steps}")
+    h = bench_rdfft(rows, p, "f32", args.steps, args.warmup, syn.WL_RDFFT_512)
+    achieved = h["bytes_per_launch"] / (h["fwd_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(h["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": h["steps"],
+        "warmup": h["warmup"],
+        "ms_per_step": round(h["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"rdFFT {rows} rows x p={p}, fp32, forward then inverse in place",
+            "rows": rows,
+            "p": p,
+            "rotating_buffers": h["nbuf"],
+            "launch": "HIP graph replays of the rotating set",
+            "roundtrip_drift": h["roundtrip_drift"],
+            "pct_hbm_peak": round(100 * h["gbs"] / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(f"rdfft_fwd_kernel<512, F32Io> {rows}x{p}"),
+            "kernel": "rdfft_fwd_kernel<512, F32Io>",
+            "kernel_ms": round(h["fwd_ms"], 6),
+            "inverse_kernel_ms": round(h["inv_ms"], 6),
+        },
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_rdfft(rows, p, args.cpu_seconds)
+    if not args.no_extra:
+        extra = {}
+        for (r, pp, dt) in ((4096, 4096, "f32"), (4096, 4096, "bf16"), (16384, 128, "f32"), (16384, 128, "bf16")):
+            log(f"extra: rdfft {r}x{pp} {dt}")
+            e = bench_rdfft(r, pp, dt, max(256, args.steps // 4), max(32, args.warmup // 4), syn.WL_RDFFT_LARGE)
+            ach = e["bytes_per_launch"] / (e["fwd_ms"] * 1e-3) / 1e9
+            extra[f"rdfft_{r}x{pp}_{dt}"] = {
+                "gbs_fwd_plus_inv": round(e["gbs"], 1),
+                "pct_hbm_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 2),
+                "fwd_kernel_gbs": round(ach, 1),
+                "fwd_kernel_ms": round(e["fwd_ms"], 5),
+                "inv_kernel_ms": round(e["inv_ms"], 5),
+            }
+        for pp in (128, 512, 4096):
+            log(f"extra: circulant layer D=4096 B=256 p={pp}")
+            extra[f"circulant_d4096_b256_p{pp}_bf16"] = bench_circ_layer(256, 4096, pp, 256, 32)
+        log("extra: 128 circulant adapters 4096x4096 p=1024, 2048 tokens")
+        extra["circulant_128_adapters_d4096_p1024_b2048_bf16"] = bench_circ_adapters(10, 2)
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

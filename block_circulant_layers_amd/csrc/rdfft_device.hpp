@@ -29,11 +29,17 @@
 //     class k) runs those log2(R) stages in registers.  Class k = 0 holds the
 //     slots 0 and B/2 of each sub-spectrum (an R-point real transform plus a
 //     half-bin-shifted one, all with constant twiddles).
-//   * between passes the row goes through LDS in a padded residue-major layout
-//     A(r, s) = r*(B+1) + s (the +1 keeps row-strided accesses off one bank).
-//   * the last pass stores the natural packed layout directly (coalesced).
-// Twiddles: one table load per stage per item (W_m^k), the others of the item
-// derived by multiplication with compile-time constants; the constants fold.
+//   * between passes the row goes through LDS in a padded residue-major
+//     layout A(r, s) = r*(B + pad) + s; the paddings and the item-to-lane
+//     order of every pass are chosen so that the 32-lane LDS accesses hit
+//     distinct banks (checked against the bank-conflict counter).
+//   * the last forward pass stores the natural packed layout directly; the
+//     first inverse pass reads it directly (both coalesced).
+// Twiddles: every item reads the R-1 twiddles of its groups from a per-pass
+// table laid out [class][group], so a wave's lanes read one contiguous block
+// with 16-byte loads.  The forward table holds (cos, tan): the group is
+// evaluated as t = c (O_re + tan O_im, O_im - tan O_re), E +- t, which needs
+// 6 instead of 8 VALU operations; the inverse table holds (cos, sin).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,6 +49,9 @@ namespace rdfft {
 
 struct Tw {
   float c, s;  // W = c - i s   (c = cos(theta), s = sin(theta), W = exp(-i theta))
+};
+struct TwF {
+  float c, tn;  // W = c (1 - i tn), tn = tan(theta)
 };
 
 #include "twiddles.inc"
@@ -58,37 +67,25 @@ __host__ __device__ constexpr int bitrev(int v, int bits) {
   return r;
 }
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Twiddle of angle 2 pi * num / den, 0 <= num/den <= 1/4, from the table.
 __device__ __forceinline__ Tw tw_const(int num, int den) { return kTw[num * (kTwN / den)]; }
-
-// angle(w) + alpha, alpha = 2 pi num / den constant in [0, pi/2]
-__device__ __forceinline__ Tw tw_add(Tw w, int num, int den) {
-  if (num == 0) return w;
-  if (4 * num == den) return Tw{-w.s, w.c};
-  const Tw a = tw_const(num, den);
-  return Tw{a.c * w.c - a.s * w.s, a.c * w.s + a.s * w.c};
-}
-// alpha - angle(w), alpha = 2 pi num / den constant in (0, pi/2]
-__device__ __forceinline__ Tw tw_sub_from(int num, int den, Tw w) {
-  if (4 * num == den) return Tw{w.s, w.c};
-  const Tw a = tw_const(num, den);
-  return Tw{a.c * w.c + a.s * w.s, a.s * w.c - a.c * w.s};
-}
+__device__ __forceinline__ TwF twf_const(int num, int den) { return kTwF[num * (kTwN / den)]; }
 
 // ---------------------------------------------------------------------------
 // the pages' in-place operations on one four-element group
 // slots (g+k, g+m/2-k, g+m/2+k, g+m-k) = (a1, a2, a3, a4)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void grp_fwd(float& a1, float& a2, float& a3, float& a4, Tw w) {
-  // in: (Re E, Im E, Re O, Im O);  t = W O with W = c - i s
-  const float tr = w.c * a3 + w.s * a4;
-  const float ti = w.c * a4 - w.s * a3;
+__device__ __forceinline__ void grp_fwd(float& a1, float& a2, float& a3, float& a4, TwF w) {
+  // in: (Re E, Im E, Re O, Im O);  t = W O = c (u + i v), u = ReO + tan ImO, v = ImO - tan ReO
+  const float u = __builtin_fmaf(w.tn, a4, a3);
+  const float v = __builtin_fmaf(-w.tn, a3, a4);
   const float er = a1, ei = a2;
-  a1 = er + tr;  // Re y_k
-  a2 = er - tr;  // Re y_{m/2-k} = Re(E - t)
-  a3 = ti - ei;  // Im y_{m/2-k} = -Im(E - t)
-  a4 = ei + ti;  // Im y_k
+  a1 = __builtin_fmaf(w.c, u, er);   // Re y_k       = Re(E + t)
+  a2 = __builtin_fmaf(-w.c, u, er);  // Re y_{m/2-k} = Re(E - t)
+  a3 = __builtin_fmaf(w.c, v, -ei);  // Im y_{m/2-k} = -Im(E - t)
+  a4 = __builtin_fmaf(w.c, v, ei);   // Im y_k       = Im(E + t)
 }
 
 __device__ __forceinline__ void grp_inv(float& a1, float& a2, float& a3, float& a4, Tw w) {
@@ -119,7 +116,7 @@ __device__ __forceinline__ void small_fwd(float* a) {
 #pragma unroll
       for (int k = 1; k < m / 4; ++k)
         grp_fwd(a[S * (g + k)], a[S * (g + m / 2 - k)], a[S * (g + m / 2 + k)], a[S * (g + m - k)],
-                tw_const(k, m));
+                twf_const(k, m));
     }
   }
 }
@@ -148,41 +145,60 @@ __device__ __forceinline__ void small_inv(float* a) {
 // ---------------------------------------------------------------------------
 // item of a pass (input spectra of size B, radix R), class 0 < k < B/2.
 // a[2q] = slot qB + k, a[2q+1] = slot qB + B - k of the (B*R)-block, q < R.
-// Stage s (m = 2B 2^s) holds, per m-block (q in [base, base + 2^(s+1))),
-// the groups kappa = k + B i and kappa = B(i+1) - k, i < 2^(s-1)
-// (only kappa = k when s = 0).
+// Stage s (m = 2B 2^s, h = 2^s) holds, per m-block (q in [base, base + 2h)),
+// the groups kappa = k + B i ("type A") and kappa = B(i+1) - k ("type B"),
+// i < h/2 (only kappa = k when s = 0):
+//   type A slots (first q=base+i, mirror base+h-i-1, first base+h+i, mirror base+2h-i-1)
+//   type B slots (mirror base+i, first base+h-i-1, mirror base+h+i, first base+2h-i-1)
 // ---------------------------------------------------------------------------
-template <int B, int R, bool INV>
-__device__ __forceinline__ void item_stage(float* a, int s, Tw w) {
-  const int nblk = R >> (s + 1);
+// per-pass twiddle tables: the R-1 group twiddles of class k at [k*R, k*R + R-1)
+template <int B, int R>
+struct PassTw;
+#define RDFFT_PASS_TW(B_, R_)                                                          \
+  template <>                                                                          \
+  struct PassTw<B_, R_> {                                                              \
+    static __device__ __forceinline__ const TwF* fwd() { return kPassF_##B_##_##R_; } \
+    static __device__ __forceinline__ const Tw* inv() { return kPassI_##B_##_##R_; }  \
+  };
+RDFFT_PASS_TW(16, 2)
+RDFFT_PASS_TW(16, 4)
+RDFFT_PASS_TW(16, 8)
+RDFFT_PASS_TW(128, 2)
+RDFFT_PASS_TW(128, 4)
+RDFFT_PASS_TW(128, 8)
+RDFFT_PASS_TW(1024, 2)
+RDFFT_PASS_TW(1024, 4)
+#undef RDFFT_PASS_TW
+
+// the R-1 twiddles of an item, read as R/2 aligned 16-byte loads
+template <class W, int R>
+__device__ __forceinline__ void load_item_tw(const W* tab, int k, W (&w)[R]) {
+  static_assert(sizeof(W) == 8 && R % 2 == 0, "twiddles are pairs of floats");
+  __builtin_memcpy(w, tab + k * R, sizeof(w));
+}
+
+template <int B, int R>
+__device__ __forceinline__ void item_fwd(float* a, int k) {
+  constexpr int NS = ilog2(R);
+  TwF w[R];
+  load_item_tw(PassTw<B, R>::fwd(), k, w);
 #pragma unroll
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int base = blk << (s + 1);
+  for (int s = 0; s < NS; ++s) {
     const int h = 1 << s;
-    if (s == 0) {
-      if (INV)
-        grp_inv(a[2 * base], a[2 * base + 1], a[2 * base + 2], a[2 * base + 3], w);
-      else
-        grp_fwd(a[2 * base], a[2 * base + 1], a[2 * base + 2], a[2 * base + 3], w);
-    } else {
+    const int j0 = h - 1;  // first twiddle of stage s
 #pragma unroll
-      for (int i = 0; i < h / 2; ++i) {
-        const Tw wa = tw_add(w, i, 2 * h);            // W_m^(k + B i)
-        const Tw wb = tw_sub_from(i + 1, 2 * h, w);   // W_m^(B(i+1) - k)
-        float& f1 = a[2 * (base + i)];
-        float& m1 = a[2 * (base + i) + 1];
-        float& f2 = a[2 * (base + h - i - 1)];
-        float& m2 = a[2 * (base + h - i - 1) + 1];
-        float& f3 = a[2 * (base + h + i)];
-        float& m3 = a[2 * (base + h + i) + 1];
-        float& f4 = a[2 * (base + 2 * h - i - 1)];
-        float& m4 = a[2 * (base + 2 * h - i - 1) + 1];
-        if (INV) {
-          grp_inv(f1, m2, f3, m4, wa);
-          grp_inv(m1, f2, m3, f4, wb);
-        } else {
-          grp_fwd(f1, m2, f3, m4, wa);
-          grp_fwd(m1, f2, m3, f4, wb);
+    for (int blk = 0; blk < (R >> (s + 1)); ++blk) {
+      const int base = blk << (s + 1);
+      if (s == 0) {
+        grp_fwd(a[2 * base], a[2 * base + 1], a[2 * base + 2], a[2 * base + 3], w[0]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < h / 2; ++i) {
+          // W_m^(k + B i) and W_m^(B(i+1) - k)
+          grp_fwd(a[2 * (base + i)], a[2 * (base + h - i - 1) + 1], a[2 * (base + h + i)],
+                  a[2 * (base + 2 * h - i - 1) + 1], w[j0 + 2 * i]);
+          grp_fwd(a[2 * (base + i) + 1], a[2 * (base + h - i - 1)], a[2 * (base + h + i) + 1],
+                  a[2 * (base + 2 * h - i - 1)], w[j0 + 2 * i + 1]);
         }
       }
     }
@@ -190,24 +206,29 @@ __device__ __forceinline__ void item_stage(float* a, int s, Tw w) {
 }
 
 template <int B, int R>
-__device__ __forceinline__ void item_fwd(float* a, int k) {
-  constexpr int NS = ilog2(R);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int lm = ilog2(2 * B) + s;  // log2 of the stage size m
-    const Tw w = kTw[k << (12 - lm)];  // W_m^k, k/m < 1/4
-    item_stage<B, R, false>(a, s, w);
-  }
-}
-
-template <int B, int R>
 __device__ __forceinline__ void item_inv(float* a, int k) {
   constexpr int NS = ilog2(R);
+  Tw w[R];
+  load_item_tw(PassTw<B, R>::inv(), k, w);
 #pragma unroll
   for (int s = NS - 1; s >= 0; --s) {
-    const int lm = ilog2(2 * B) + s;
-    const Tw w = kTw[k << (12 - lm)];
-    item_stage<B, R, true>(a, s, w);
+    const int h = 1 << s;
+    const int j0 = h - 1;
+#pragma unroll
+    for (int blk = 0; blk < (R >> (s + 1)); ++blk) {
+      const int base = blk << (s + 1);
+      if (s == 0) {
+        grp_inv(a[2 * base], a[2 * base + 1], a[2 * base + 2], a[2 * base + 3], w[0]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < h / 2; ++i) {
+          grp_inv(a[2 * (base + i)], a[2 * (base + h - i - 1) + 1], a[2 * (base + h + i)],
+                  a[2 * (base + 2 * h - i - 1) + 1], w[j0 + 2 * i]);
+          grp_inv(a[2 * (base + i) + 1], a[2 * (base + h - i - 1)], a[2 * (base + h + i) + 1],
+                  a[2 * (base + 2 * h - i - 1)], w[j0 + 2 * i + 1]);
+        }
+      }
+    }
   }
 }
 
@@ -216,13 +237,12 @@ __device__ __forceinline__ void item_inv(float* a, int k) {
 // W_m^kappa = W_(2^(s+2))^(2c+1); at s = 0 only the quarter-pair negation).
 template <int R, bool INV>
 __device__ __forceinline__ void item0_odd_stage(float* a, int s) {
-  const int nblk = R >> (s + 1);
+  const int h = 1 << s;
 #pragma unroll
-  for (int blk = 0; blk < nblk; ++blk) {
+  for (int blk = 0; blk < (R >> (s + 1)); ++blk) {
     const int base = blk << (s + 1);
-    const int h = 1 << s;
     if (s == 0) {
-      // quarter pair of stage 2B: slot g + 3B/2 = a[2(base+1)+1]
+      // quarter pair of stage 2B: slots g + B/2 (a[2 base + 1]) and g + 3B/2 (a[2 base + 3])
       if (INV) {
         a[2 * base + 1] = 2.0f * a[2 * base + 1];
         a[2 * base + 3] = -2.0f * a[2 * base + 3];
@@ -232,15 +252,14 @@ __device__ __forceinline__ void item0_odd_stage(float* a, int s) {
     } else {
 #pragma unroll
       for (int c = 0; c < h / 2; ++c) {
-        const Tw w = tw_const(2 * c + 1, 4 * h);
         float& a1 = a[2 * (base + c) + 1];
         float& a2 = a[2 * (base + h - c - 1) + 1];
         float& a3 = a[2 * (base + h + c) + 1];
         float& a4 = a[2 * (base + 2 * h - c - 1) + 1];
         if (INV)
-          grp_inv(a1, a2, a3, a4, w);
+          grp_inv(a1, a2, a3, a4, tw_const(2 * c + 1, 4 * h));
         else
-          grp_fwd(a1, a2, a3, a4, w);
+          grp_fwd(a1, a2, a3, a4, twf_const(2 * c + 1, 4 * h));
       }
     }
   }
@@ -261,36 +280,75 @@ __device__ __forceinline__ void item0_inv(float* a) {
 }
 
 // ---------------------------------------------------------------------------
-// storage types
+// storage types and buffer-resource access
 // ---------------------------------------------------------------------------
+// A buffer resource covers [base, base + nbytes): loads past the end return
+// 0 and stores past the end are dropped by the hardware, so rows beyond the
+// last one need no branches.  voff is the lane-varying byte offset, soff a
+// wave-uniform one.
+constexpr int kBufWord3 = 0x00020000;
+
 struct F32Io {
   using T = float;
   static __device__ __forceinline__ float load(const float* p) { return *p; }
   static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff * 4, soff * 4, 0));
+  }
+  static __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff * 4, soff * 4, 0);
+  }
 };
 struct Bf16Io {
   using T = uint16_t;
-  static __device__ __forceinline__ float load(const uint16_t* p) {
-    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  static __device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+  static __device__ __forceinline__ uint16_t narrow(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
   }
-  static __device__ __forceinline__ void store(uint16_t* p, float v) {
-    *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+  static __device__ __forceinline__ float load(const uint16_t* p) { return widen(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = narrow(v); }
+  static __device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return widen(__builtin_amdgcn_raw_buffer_load_b16(r, voff * 2, soff * 2, 0));
+  }
+  static __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(narrow(v), r, voff * 2, soff * 2, 0);
   }
 };
 
+template <class Io>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const typename Io::T* base, int64_t elems) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<typename Io::T*>(base), 0,
+                                           static_cast<int>(elems * sizeof(typename Io::T)), kBufWord3);
+}
+
 // ---------------------------------------------------------------------------
-// one row of P reals, T = P/E threads (t = thread index within the row)
+// exchange layouts: padding of layout B and item order of the pass reading
+// layout B, for rows of P with E = 16 per thread.  Chosen by simulating the
+// 32-bank conflicts of every LDS access of the pass schedule.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int lds_pad(int P, int B) {
+  return B <= 16 ? 1 : B == 128 ? (P <= 512 ? 8 : P == 1024 ? 4 : P == 2048 ? 2 : 1) : 0;
+}
+// true: items of the pass with input size B are numbered class-fastest
+// (k = item % (B/2)); false: residue-fastest (r' = item % NRES)
+__host__ __device__ constexpr bool class_fast(int P, int B) { return B == 128 && P >= 2048; }
+
+// ---------------------------------------------------------------------------
+// one row of P reals, T = P/E threads (t = thread index within the row).
+// Loaders are called as ld(var, cst) for element var + cst (var varies per
+// lane, cst is a compile-time constant); storers as st(var, cst, value).
 // ---------------------------------------------------------------------------
 template <int P, int E>
 struct Row {
   static_assert((P & (P - 1)) == 0 && P >= 2 && P <= 4096, "P must be a power of two in [2, 4096]");
   static_assert(E <= P && (E & (E - 1)) == 0 && E >= 2, "E must be a power of two <= P");
   static constexpr int T = P / E;
-  static constexpr int LDS = P + T;  // floats of LDS a row needs (largest padded layout)
 
+  template <int B>
+  static constexpr int stride() { return B + lds_pad(P, B); }
   // layout of an exchange whose spectra have size B: residue r, slot s
   template <int B>
-  static __device__ __forceinline__ int addr(int r, int s) { return r * (B + 1) + s; }
+  static __device__ __forceinline__ int addr(int r, int s) { return r * stride<B>() + s; }
 
   // pass descriptors, input size B
   template <int B>
@@ -299,15 +357,35 @@ struct Row {
     static constexpr int BP = B * R;
     static constexpr int NRES = P / BP;
     static constexpr int IPT = E / (2 * R);
+    static constexpr bool KFAST = class_fast(P, B);
+    static __device__ __forceinline__ void item(int it, int& rp, int& k) {
+      if (KFAST) {
+        k = it % (B / 2);
+        rp = it / (B / 2);
+      } else {
+        rp = it % NRES;
+        k = it / NRES;
+      }
+    }
   };
 
+  // floats of LDS a row needs: the largest exchange layout
+  template <int B>
+  static constexpr int lds_from() {
+    if constexpr (B >= P)
+      return P;
+    else
+      return cmax((P / B) * stride<B>(), lds_from<Pass<B>::BP>());
+  }
+  static constexpr int LDS = (P == E) ? P : lds_from<E>();
+
   // ---- forward ----------------------------------------------------------
-  // pass 0: ld(i) returns x[i]; thread t reads i = t + T*s (coalesced across threads)
+  // pass 0: thread t reads elements t + T*s (coalesced across threads)
   template <class Ld>
   static __device__ __forceinline__ void fwd_pass0(float (&a)[E], Ld ld, int t) {
     constexpr int LE = ilog2(E);
 #pragma unroll
-    for (int s = 0; s < E; ++s) a[bitrev(s, LE)] = ld(t + T * s);
+    for (int s = 0; s < E; ++s) a[bitrev(s, LE)] = ld(t, T * s);
     small_fwd<E, 1>(a);
   }
 
@@ -323,8 +401,8 @@ struct Row {
     constexpr int R = PS::R, LR = ilog2(R);
 #pragma unroll
     for (int n = 0; n < PS::IPT; ++n) {
-      const int it = t + T * n;
-      const int rp = it % PS::NRES, k = it / PS::NRES;
+      int rp, k;
+      PS::item(t + T * n, rp, k);
       const int k2 = (k == 0) ? (B / 2) : (B - k);
       float* v = a + 2 * R * n;
 #pragma unroll
@@ -340,15 +418,15 @@ struct Row {
     }
   }
 
-  // write the items of pass B to LDS in layout B*R
+  // write the items of pass B to LDS in layout B*R (natural order when B*R == P)
   template <int B>
   static __device__ __forceinline__ void pass_scatter(const float (&a)[E], float* L, int t) {
     using PS = Pass<B>;
     constexpr int R = PS::R;
 #pragma unroll
     for (int n = 0; n < PS::IPT; ++n) {
-      const int it = t + T * n;
-      const int rp = it % PS::NRES, k = it / PS::NRES;
+      int rp, k;
+      PS::item(t + T * n, rp, k);
       const int k2 = (k == 0) ? (B / 2) : (B - k);
       const float* v = a + 2 * R * n;
 #pragma unroll
@@ -359,7 +437,7 @@ struct Row {
     }
   }
 
-  // store the items of the last pass (B*R == P) in natural packed order: st(slot, value)
+  // store the items of the last pass (B*R == P) in natural packed order
   template <int B, class St>
   static __device__ __forceinline__ void last_store(const float (&a)[E], int t, St st) {
     using PS = Pass<B>;
@@ -372,29 +450,30 @@ struct Row {
       const float* v = a + 2 * R * n;
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        st(q * B + k, v[2 * q]);
-        st(q * B + k2, v[2 * q + 1]);
+        st(k, q * B, v[2 * q]);
+        st(k2, q * B, v[2 * q + 1]);
       }
     }
   }
 
   // ---- inverse -----------------------------------------------------------
-  // gather items of inverse pass B (input spectra of size B*R) from `src`
-  // (LDS in layout B*R, or global natural packed when B*R == P) and run it
+  // gather items of inverse pass B (input spectra of size B*R) through
+  // src(var, cst) -- LDS in layout B*R, or the natural packed row when
+  // B*R == P -- and run it
   template <int B, class Src>
   static __device__ __forceinline__ void inv_pass(float (&a)[E], Src src, int t) {
     using PS = Pass<B>;
     constexpr int R = PS::R;
 #pragma unroll
     for (int n = 0; n < PS::IPT; ++n) {
-      const int it = t + T * n;
-      const int rp = it % PS::NRES, k = it / PS::NRES;
+      int rp, k;
+      PS::item(t + T * n, rp, k);
       const int k2 = (k == 0) ? (B / 2) : (B - k);
       float* v = a + 2 * R * n;
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        v[2 * q] = src(addr<PS::BP>(rp, q * B + k));
-        v[2 * q + 1] = src(addr<PS::BP>(rp, q * B + k2));
+        v[2 * q] = src(addr<PS::BP>(rp, k), q * B);
+        v[2 * q + 1] = src(addr<PS::BP>(rp, k2), q * B);
       }
       if (k == 0)
         item0_inv<R>(v);
@@ -410,8 +489,8 @@ struct Row {
     constexpr int R = PS::R, LR = ilog2(R);
 #pragma unroll
     for (int n = 0; n < PS::IPT; ++n) {
-      const int it = t + T * n;
-      const int rp = it % PS::NRES, k = it / PS::NRES;
+      int rp, k;
+      PS::item(t + T * n, rp, k);
       const int k2 = (k == 0) ? (B / 2) : (B - k);
       const float* v = a + 2 * R * n;
 #pragma unroll
@@ -424,7 +503,7 @@ struct Row {
   }
 
   // inverse pass 0: gather residue t's E-point spectrum from LDS (layout E),
-  // invert, store x[t + T s] = value * scale through st(i, v)
+  // invert, store element t + T s = value * scale through st(var, cst, v)
   template <class St>
   static __device__ __forceinline__ void inv_pass0_store(float (&a)[E], const float* L, int t, float scale, St st) {
     constexpr int LE = ilog2(E);
@@ -432,7 +511,7 @@ struct Row {
     for (int s = 0; s < E; ++s) a[s] = L[addr<E>(t, s)];
     small_inv<E, 1>(a);
 #pragma unroll
-    for (int s = 0; s < E; ++s) st(t + T * s, a[bitrev(s, LE)] * scale);
+    for (int s = 0; s < E; ++s) st(t, T * s, a[bitrev(s, LE)] * scale);
   }
 };
 

@@ -51,3 +51,21 @@ def cast_like_device(a: np.ndarray, dtype: str):
     else:
         raise ValueError(f"unknown dtype {dtype!r}")
     return tt, tt.to(torch.float64).numpy()
+
+
+def torch_normal(shape, workload: int, tensor: int, index: int = 0, scale: float = 1.0, dtype=None, device="cuda:0"):
+    """N(0, scale^2) tensor drawn on `device` by torch's Philox generator seeded
+    from (workload, tensor, index); used for the large benchmark buffers where
+    drawing float64 on the host would dominate the run.  The oracle side of a
+    comparison reads back the same device values."""
+    import torch
+
+    seed = int(np.random.SeedSequence([int(workload), int(tensor), int(index)]).generate_state(1, np.uint64)[0]) & (
+        (1 << 63) - 1
+    )
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        t.mul_(scale)
+    return t if dtype is None else t.to(dtype)

@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 import block_circulant_layers_amd as bcl  # noqa: E402
 from block_circulant_layers_amd import synthetic as syn  # noqa: E402
 
+IO_NAME = {"f32": "F32Io", "bf16": "Bf16Io"}
 METRIC = "rdFFT GB/s + % HBM peak (p=512,4096); circulant fwd+bwd tokens/s"
 HBM_PEAK_GBS = 8000.0
 VALU_FP32_PEAK_TFS = 157.3
@@ -50,14 +51,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TRANSFORM_SOURCES = ("rdfft_device.hpp", "rdfft_kernels.hpp", "gen_twiddles.py")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources; traffic figures taken from counters are only
-    reported while the kernels they were measured on are unchanged."""
+    """Hash of the transform kernels' sources; traffic figures taken from
+    counters are only reported while the kernels they were measured on are
+    unchanged."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hpp", ".hip")):
-            with open(os.path.join(CSRC, name), "rb") as fh:
-                h.update(name.encode() + fh.read())
+    for name in TRANSFORM_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -274,6 +278,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--rows", type=int, default=4096, help="transform rows of the timed workload")
+    ap.add_argument("--p", type=int, default=512, help="row length of the timed workload")
+    ap.add_argument("--dtype", choices=("f32", "bf16"), default="f32", help="storage type of the timed workload")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -297,9 +304,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    rows, p = 4096, 512
-    log(f"headline: rdfft {rows}x{p} f32 fwd+inv, warmup {args.warmup}, steps {args.steps}")
-    h = bench_rdfft(rows, p, "f32", args.steps, args.warmup, syn.WL_RDFFT_512)
+    rows, p, dt = args.rows, args.p, args.dtype
+    log(f"headline: rdfft {rows}x{p} {dt} fwd+inv, warmup {args.warmup}, steps {args.steps}")
+    wl = syn.WL_RDFFT_512 if (rows, p) == (4096, 512) else syn.WL_RDFFT_LARGE
+    h = bench_rdfft(rows, p, dt, args.steps, args.warmup, wl)
     achieved = h["bytes_per_launch"] / (h["fwd_ms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -312,10 +320,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": f"rdFFT {rows} rows x p={p}, fp32, forward then inverse in place",
+            "workload": f"rdFFT {rows} rows x p={p}, {dt}, forward then inverse in place",
             "rows": rows,
             "p": p,
             "rotating_buffers": h["nbuf"],
@@ -329,13 +337,13 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(f"rdfft_fwd_kernel<512, F32Io> {rows}x{p}"),
-            "kernel": "rdfft_fwd_kernel<512, F32Io>",
+            "traffic": recorded_traffic(f"rdfft_fwd_kernel<{p}, {IO_NAME[dt]}> {rows}x{p}"),
+            "kernel": f"rdfft_fwd_kernel<{p}, {IO_NAME[dt]}>",
             "kernel_ms": round(h["fwd_ms"], 6),
             "inverse_kernel_ms": round(h["inv_ms"], 6),
         },
     }
-    if not args.no_cpu:
+    if not args.no_cpu and (rows, p, dt) == (4096, 512, "f32"):
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline_rdfft(rows, p, args.cpu_seconds)
     if not args.no_extra:

@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rdfft {
 
 struct Tw {
@@ -178,10 +180,8 @@ __device__ __forceinline__ void load_item_tw(const W* tab, int k, W (&w)[R]) {
 }
 
 template <int B, int R>
-__device__ __forceinline__ void item_fwd(float* a, int k) {
+__device__ __forceinline__ void item_fwd(float* a, const TwF (&w)[R]) {
   constexpr int NS = ilog2(R);
-  TwF w[R];
-  load_item_tw(PassTw<B, R>::fwd(), k, w);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int h = 1 << s;
@@ -206,10 +206,8 @@ __device__ __forceinline__ void item_fwd(float* a, int k) {
 }
 
 template <int B, int R>
-__device__ __forceinline__ void item_inv(float* a, int k) {
+__device__ __forceinline__ void item_inv(float* a, const Tw (&w)[R]) {
   constexpr int NS = ilog2(R);
-  Tw w[R];
-  load_item_tw(PassTw<B, R>::inv(), k, w);
 #pragma unroll
   for (int s = NS - 1; s >= 0; --s) {
     const int h = 1 << s;
@@ -290,6 +288,10 @@ constexpr int kBufWord3 = 0x00020000;
 
 struct F32Io {
   using T = float;
+  static __device__ __forceinline__ float widen(float v) { return v; }
+  static __device__ __forceinline__ float braw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff * 4, soff * 4, 0));
+  }
   static __device__ __forceinline__ float load(const float* p) { return *p; }
   static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
   static __device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -304,6 +306,9 @@ struct Bf16Io {
   static __device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
   static __device__ __forceinline__ uint16_t narrow(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+  }
+  static __device__ __forceinline__ uint16_t braw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff * 2, soff * 2, 0);
   }
   static __device__ __forceinline__ float load(const uint16_t* p) { return widen(*p); }
   static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = narrow(v); }
@@ -379,6 +384,42 @@ struct Row {
   }
   static constexpr int LDS = (P == E) ? P : lds_from<E>();
 
+  // Twiddles of this thread's items in every pass with input size >= B, read
+  // once per kernel (they depend on the thread only) and kept in registers.
+  template <int B, bool INV, bool END = (B >= P)>
+  struct Tws {
+    using PS = Pass<B>;
+    using W = typename std::conditional<INV, Tw, TwF>::type;
+    W w[PS::IPT][PS::R];
+    Tws<PS::BP, INV> next;
+    __device__ __forceinline__ void load(int t) {
+#pragma unroll
+      for (int n = 0; n < PS::IPT; ++n) {
+        int rp, k;
+        PS::item(t + T * n, rp, k);
+        if constexpr (INV)
+          load_item_tw(PassTw<B, PS::R>::inv(), k, w[n]);
+        else
+          load_item_tw(PassTw<B, PS::R>::fwd(), k, w[n]);
+      }
+      next.load(t);
+    }
+    // the twiddles of the pass with input size B2 >= B
+    template <int B2>
+    __device__ __forceinline__ const auto& at() const {
+      if constexpr (B2 == B)
+        return w;
+      else
+        return next.template at<B2>();
+    }
+  };
+  template <int B, bool INV>
+  struct Tws<B, INV, true> {
+    __device__ __forceinline__ void load(int) {}
+  };
+  using FwdTws = Tws<E, false>;
+  using InvTws = Tws<E, true>;
+
   // ---- forward ----------------------------------------------------------
   // pass 0: thread t reads elements t + T*s (coalesced across threads)
   template <class Ld>
@@ -388,6 +429,20 @@ struct Row {
     for (int s = 0; s < E; ++s) a[bitrev(s, LE)] = ld(t, T * s);
     small_fwd<E, 1>(a);
   }
+  // the same split in two: the loads (raw values, possibly a row ahead) ...
+  template <class V, class Ld>
+  static __device__ __forceinline__ void fwd_load0(V (&raw)[E], Ld ld, int t) {
+#pragma unroll
+    for (int s = 0; s < E; ++s) raw[s] = ld(t, T * s);
+  }
+  // ... and the stages
+  template <class V, class Wd>
+  static __device__ __forceinline__ void fwd_pass0_from(float (&a)[E], const V (&raw)[E], Wd widen) {
+    constexpr int LE = ilog2(E);
+#pragma unroll
+    for (int s = 0; s < E; ++s) a[bitrev(s, LE)] = widen(raw[s]);
+    small_fwd<E, 1>(a);
+  }
 
   static __device__ __forceinline__ void fwd_pass0_scatter(const float (&a)[E], float* L, int t) {
 #pragma unroll
@@ -395,8 +450,8 @@ struct Row {
   }
 
   // gather items of the pass with input size B from LDS (layout B) and run it
-  template <int B>
-  static __device__ __forceinline__ void fwd_pass(float (&a)[E], const float* L, int t) {
+  template <int B, class W>
+  static __device__ __forceinline__ void fwd_pass(float (&a)[E], const float* L, int t, const W& tw) {
     using PS = Pass<B>;
     constexpr int R = PS::R, LR = ilog2(R);
 #pragma unroll
@@ -414,7 +469,7 @@ struct Row {
       if (k == 0)
         item0_fwd<R>(v);
       else
-        item_fwd<B, R>(v, k);
+        item_fwd<B, R>(v, tw[n]);
     }
   }
 
@@ -460,8 +515,8 @@ struct Row {
   // gather items of inverse pass B (input spectra of size B*R) through
   // src(var, cst) -- LDS in layout B*R, or the natural packed row when
   // B*R == P -- and run it
-  template <int B, class Src>
-  static __device__ __forceinline__ void inv_pass(float (&a)[E], Src src, int t) {
+  template <int B, class Src, class W>
+  static __device__ __forceinline__ void inv_pass(float (&a)[E], Src src, int t, const W& tw) {
     using PS = Pass<B>;
     constexpr int R = PS::R;
 #pragma unroll
@@ -478,8 +533,52 @@ struct Row {
       if (k == 0)
         item0_inv<R>(v);
       else
-        item_inv<B, R>(v, k);
+        item_inv<B, R>(v, tw[n]);
     }
+  }
+
+  // the first inverse pass (B*R == P) split in two: the loads of the natural
+  // packed row (raw values, possibly a row ahead) ...
+  template <int B, class V, class Ld>
+  static __device__ __forceinline__ void inv_load_first(V (&raw)[E], Ld ld, int t) {
+    using PS = Pass<B>;
+    static_assert(PS::BP == P, "not the first inverse pass");
+    constexpr int R = PS::R;
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int k = t + T * n;
+      const int k2 = (k == 0) ? (B / 2) : (B - k);
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        raw[2 * R * n + 2 * q] = ld(k, q * B);
+        raw[2 * R * n + 2 * q + 1] = ld(k2, q * B);
+      }
+    }
+  }
+  // ... and its stages
+  template <int B, class V, class Wd, class W>
+  static __device__ __forceinline__ void inv_first_from(float (&a)[E], const V (&raw)[E], Wd widen, int t,
+                                                        const W& tw) {
+    using PS = Pass<B>;
+    constexpr int R = PS::R;
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      const int k = t + T * n;
+      float* v = a + 2 * R * n;
+#pragma unroll
+      for (int j = 0; j < 2 * R; ++j) v[j] = widen(raw[2 * R * n + j]);
+      if (k == 0)
+        item0_inv<R>(v);
+      else
+        item_inv<B, R>(v, tw[n]);
+    }
+  }
+
+  // input size of the pass whose output size is Bout (Bout > E)
+  static constexpr int pass_in_for(int Bout) {
+    int b = E;
+    while (b * cmin(P / b, E / 2) != Bout) b *= cmin(P / b, E / 2);
+    return b;
   }
 
   // write the items of inverse pass B to LDS in layout B

@@ -16,54 +16,72 @@ namespace rdfft {
 __host__ __device__ constexpr int elems_per_thread(int P) { return P < 16 ? P : 16; }
 // threads per workgroup of the standalone kernels: at least 256, or one whole row
 __host__ __device__ constexpr int wg_threads(int P, int E) { return (P / E) > 256 ? (P / E) : 256; }
+// resident workgroups per CU the standalone kernels are launched for
+__host__ __device__ constexpr int wg_per_cu(int P) { return P >= 1024 ? 4 : 2; }
 
 // Forward passes with input spectra of size B and all later ones.  The last
 // pass either stores the natural packed row through st (global) or, when
 // TO_LDS, scatters it to L[0..P) (layout P is the natural order).
-template <int P, int E, int B, bool TO_LDS, class St>
-__device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st) {
+template <int P, int E, int B, bool TO_LDS, class St, class TW>
+__device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, const TW& tw) {
   using Rw = Row<P, E>;
   using PS = typename Rw::template Pass<B>;
   __syncthreads();  // the previous pass's scatter is visible
-  Rw::template fwd_pass<B>(a, L, t);
+  Rw::template fwd_pass<B>(a, L, t, tw.template at<B>());
   if constexpr (PS::BP == P && !TO_LDS) {
     Rw::template last_store<B>(a, t, st);
   } else {
     __syncthreads();  // every gather of this exchange is done
     Rw::template pass_scatter<B>(a, L, t);
-    if constexpr (PS::BP != P) fwd_rest<P, E, PS::BP, TO_LDS>(a, L, t, st);
+    if constexpr (PS::BP != P) fwd_rest<P, E, PS::BP, TO_LDS>(a, L, t, st, tw);
   }
 }
 
 // Inverse passes undoing forward passes B, B*R, ..., P.  The first one reads
 // the natural packed row through ld (global) or, when FROM_LDS, from L[0..P).
 // On return L holds the size-B spectra in layout B, synchronised.
-template <int P, int E, int B, bool FROM_LDS, class Ld>
-__device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld) {
+template <int P, int E, int B, bool FROM_LDS, class Ld, class TW>
+__device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld, const TW& tw) {
   using Rw = Row<P, E>;
   using PS = typename Rw::template Pass<B>;
   auto from_lds = [L](int v, int c) { return L[v + c]; };
   if constexpr (PS::BP == P) {
     if constexpr (FROM_LDS) {
-      Rw::template inv_pass<B>(a, from_lds, t);
+      Rw::template inv_pass<B>(a, from_lds, t, tw.template at<B>());
       __syncthreads();
     } else {
-      Rw::template inv_pass<B>(a, ld, t);
+      Rw::template inv_pass<B>(a, ld, t, tw.template at<B>());
     }
   } else {
-    inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld);
-    Rw::template inv_pass<B>(a, from_lds, t);
+    inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld, tw);
+    Rw::template inv_pass<B>(a, from_lds, t, tw.template at<B>());
     __syncthreads();  // every gather of this exchange is done
   }
   Rw::template inv_scatter<B>(a, L, t);
   __syncthreads();
 }
 
+// Inverse passes below the first one: on entry L holds spectra of size Bout in
+// layout Bout (synchronised); on return it holds the size-E spectra in layout E.
+template <int P, int E, int Bout, class TW>
+__device__ __forceinline__ void inv_down(float (&a)[E], float* L, int t, const TW& tw) {
+  if constexpr (Bout > E) {
+    using Rw = Row<P, E>;
+    constexpr int B = Rw::pass_in_for(Bout);
+    Rw::template inv_pass<B>(a, [L](int v, int c) { return L[v + c]; }, t, tw.template at<B>());
+    __syncthreads();  // every gather of this exchange is done
+    Rw::template inv_scatter<B>(a, L, t);
+    __syncthreads();
+    inv_down<P, E, B>(a, L, t, tw);
+  }
+}
+
 // Forward transform of one row into L[0..P) (natural packed order).
 // ld(var, cst) returns element var + cst (var = t, cst = T*s).  No barrier
 // after the final write.  Every thread of the workgroup must call it.
-template <int P, class Ld>
-__device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t) {
+// tw: the row's forward twiddles (Row<P, E>::FwdTws, loaded once by the caller).
+template <int P, class Ld, class TW>
+__device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW& tw) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   float a[E];
@@ -73,7 +91,7 @@ __device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t) {
     for (int s = 0; s < P; ++s) L[s] = a[s];
   } else {
     Rw::fwd_pass0_scatter(a, L, t);
-    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {});
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw);
   }
 }
 
@@ -81,8 +99,9 @@ __device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t) {
 // synchronised after writing it); st(var, cst, v) stores element var + cst.
 // L is used as exchange space; no barrier after the last read of L.
 // Every thread of the workgroup must call it.
-template <int P, class St>
-__device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float scale) {
+// tw: the row's inverse twiddles (Row<P, E>::InvTws, loaded once by the caller).
+template <int P, class St, class TW>
+__device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float scale, const TW& tw) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   float a[E];
@@ -94,11 +113,18 @@ __device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float s
 #pragma unroll
     for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
   } else {
-    inv_rest<P, E, E, true>(a, L, t, [](int, int) { return 0.0f; });
+    inv_rest<P, E, E, true>(a, L, t, [](int, int) { return 0.0f; }, tw);
     Rw::inv_pass0_store(a, L, t, scale, st);
   }
 }
 
+// ---------------------------------------------------------------------------
+// standalone kernels: persistent workgroups, each looping over groups of ROWS
+// rows with the next group's loads issued before the current group is
+// transformed (its values wait in registers), so loads, arithmetic and stores
+// of different groups overlap.  The twiddles depend only on the thread and
+// stay in registers across the loop.
+// ---------------------------------------------------------------------------
 template <int P, class Io>
 __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
     rdfft_fwd_kernel(typename Io::T* __restrict__ data, int64_t rows) {
@@ -110,21 +136,42 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
   const int tid = threadIdx.x;
   const int rl = tid / T, t = tid % T;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * ROWS;
-  const int64_t nrow = (rows - r0 < ROWS) ? rows - r0 : ROWS;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + r0 * P, nrow * P);
   const int ro = rl * P;
-  auto ld = [rs, ro](int v, int c) { return Io::bload(rs, ro + v, c); };
-  auto st = [rs, ro](int v, int c, float x) { Io::bstore(rs, ro + v, c, x); };
-  float a[E];
-  Rw::fwd_pass0(a, ld, t);
-  if constexpr (P == E) {
+  const int64_t ngroups = (rows + ROWS - 1) / ROWS;
+  int64_t g = blockIdx.x;
+  if (g >= ngroups) return;
+  auto rsrc = [data, rows](int64_t gg) {
+    const int64_t r0 = gg * ROWS;
+    return make_rsrc<Io>(data + r0 * P, ((rows - r0 < ROWS) ? rows - r0 : ROWS) * P);
+  };
+  typename Io::T raw[E];
+  {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(g);
+    Rw::fwd_load0(raw, [rs, ro](int v, int c) { return Io::braw(rs, ro + v, c); }, t);
+  }
+  typename Rw::FwdTws tw;
+  tw.load(t);
+  float* L = lds + rl * Rw::LDS;
+  while (true) {
+    float a[E];
+    Rw::fwd_pass0_from(a, raw, [](typename Io::T v) { return Io::widen(v); });
+    const __amdgpu_buffer_rsrc_t rs = rsrc(g);
+    const int64_t gn = g + gridDim.x;
+    if (gn < ngroups) {
+      const __amdgpu_buffer_rsrc_t rn = rsrc(gn);
+      Rw::fwd_load0(raw, [rn, ro](int v, int c) { return Io::braw(rn, ro + v, c); }, t);
+    }
+    auto st = [rs, ro](int v, int c, float x) { Io::bstore(rs, ro + v, c, x); };
+    if constexpr (P == E) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) st(0, s, a[s]);
-  } else {
-    float* L = lds + rl * Rw::LDS;
-    Rw::fwd_pass0_scatter(a, L, t);
-    fwd_rest<P, E, E, false>(a, L, t, st);
+      for (int s = 0; s < P; ++s) st(0, s, a[s]);
+    } else {
+      Rw::fwd_pass0_scatter(a, L, t);
+      fwd_rest<P, E, E, false>(a, L, t, st, tw);
+    }
+    g = gn;
+    if (g >= ngroups) break;
+    if constexpr (P != E) __syncthreads();  // the last gathers are done before LDS is reused
   }
 }
 
@@ -140,24 +187,58 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
   const int tid = threadIdx.x;
   const int rl = tid / T, t = tid % T;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * ROWS;
-  const int64_t nrow = (rows - r0 < ROWS) ? rows - r0 : ROWS;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + r0 * P, nrow * P);
   const int ro = rl * P;
-  auto ld = [rs, ro](int v, int c) { return Io::bload(rs, ro + v, c); };
-  auto st = [rs, ro](int v, int c, float x) { Io::bstore(rs, ro + v, c, x); };
-  float a[E];
-  if constexpr (P == E) {
+  const int64_t ngroups = (rows + ROWS - 1) / ROWS;
+  int64_t g = blockIdx.x;
+  if (g >= ngroups) return;
+  auto rsrc = [data, rows](int64_t gg) {
+    const int64_t r0 = gg * ROWS;
+    return make_rsrc<Io>(data + r0 * P, ((rows - r0 < ROWS) ? rows - r0 : ROWS) * P);
+  };
+  // loads of a group: the natural packed row as the first inverse pass wants it
+  auto load = [=](typename Io::T(&raw)[E], __amdgpu_buffer_rsrc_t rs) {
+    auto ld = [rs, ro](int v, int c) { return Io::braw(rs, ro + v, c); };
+    if constexpr (P == E) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) a[s] = ld(0, s);
-    small_inv<P, 1>(a);
-    constexpr int LP = ilog2(P);
+      for (int s = 0; s < P; ++s) raw[s] = ld(0, s);
+    } else {
+      Rw::template inv_load_first<Rw::pass_in_for(P)>(raw, ld, t);
+    }
+  };
+  typename Io::T raw[E];
+  load(raw, rsrc(g));
+  typename Rw::InvTws tw;
+  tw.load(t);
+  float* L = lds + rl * Rw::LDS;
+  auto widen = [](typename Io::T v) { return Io::widen(v); };
+  while (true) {
+    float a[E];
+    if constexpr (P == E) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
-  } else {
-    float* L = lds + rl * Rw::LDS;
-    inv_rest<P, E, E, false>(a, L, t, ld);
-    Rw::inv_pass0_store(a, L, t, scale, st);
+      for (int s = 0; s < P; ++s) a[s] = widen(raw[s]);
+      small_inv<P, 1>(a);
+    } else {
+      constexpr int BL = Rw::pass_in_for(P);
+      Rw::template inv_first_from<BL>(a, raw, widen, t, tw.template at<BL>());
+    }
+    const __amdgpu_buffer_rsrc_t rs = rsrc(g);
+    const int64_t gn = g + gridDim.x;
+    if (gn < ngroups) load(raw, rsrc(gn));
+    auto st = [rs, ro](int v, int c, float x) { Io::bstore(rs, ro + v, c, x); };
+    if constexpr (P == E) {
+      constexpr int LP = ilog2(P);
+#pragma unroll
+      for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
+    } else {
+      constexpr int BL = Rw::pass_in_for(P);
+      Rw::template inv_scatter<BL>(a, L, t);
+      __syncthreads();
+      inv_down<P, E, BL>(a, L, t, tw);
+      Rw::inv_pass0_store(a, L, t, scale, st);
+    }
+    g = gn;
+    if (g >= ngroups) break;
+    if constexpr (P != E) __syncthreads();  // the last gathers are done before LDS is reused
   }
 }
 

@@ -11,13 +11,28 @@ namespace {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? RDFFT_OK : RDFFT_ERR_LAUNCH; }
 
+// compute units of the current device (cached per device; 256 if the query fails)
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int P, class Io, bool INV>
 int launch_rdfft(void* data, int64_t rows, hipStream_t stream) {
   constexpr int E = elems_per_thread(P);
   constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / (P / E);
-  const int64_t grid = (rows + ROWS - 1) / ROWS;
-  if (grid > 0x7fffffff) return RDFFT_ERR_SIZE;
+  const int64_t groups = (rows + ROWS - 1) / ROWS;
+  const int64_t resident = static_cast<int64_t>(device_cus()) * wg_per_cu(P);
+  const int64_t grid = groups < resident ? groups : resident;
   auto* d = static_cast<typename Io::T*>(data);
   if (INV)
     rdfft_inv_kernel<P, Io><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(d, rows);

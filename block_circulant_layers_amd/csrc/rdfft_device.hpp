@@ -412,6 +412,13 @@ struct Row {
       else
         return next.template at<B2>();
     }
+    // twiddle provider interface: the R twiddles of item n (class k) of pass B2
+    template <int B2, class WW, int RR>
+    __device__ __forceinline__ void item(int n, int /*k*/, WW (&out)[RR]) const {
+      const auto& src = at<B2>()[n];
+#pragma unroll
+      for (int j = 0; j < RR; ++j) out[j] = src[j];
+    }
   };
   template <int B, bool INV>
   struct Tws<B, INV, true> {
@@ -419,6 +426,71 @@ struct Row {
   };
   using FwdTws = Tws<E, false>;
   using InvTws = Tws<E, true>;
+
+  // Twiddle provider reading the per-pass (cos, tan) tables from an LDS copy
+  // (for kernels that cannot keep them in registers); inverse twiddles take
+  // sin = cos * tan.
+  struct LdsTws {
+    const TwF* base;
+    template <int B>
+    static constexpr int offset() {
+      if constexpr (B == E)
+        return 0;
+      else
+        return offset<pass_in_for(B)>() + (pass_in_for(B) / 2) * Pass<pass_in_for(B)>::R;
+    }
+    static constexpr int entries() { return (P == E) ? 0 : offset<P>(); }
+    // cooperative copy of the global tables into dst (entries() values)
+    template <int B = E>
+    static __device__ __forceinline__ void fill(TwF* dst, int tid, int nt) {
+      if constexpr (B < P) {
+        constexpr int R = Pass<B>::R, N = (B / 2) * R;
+        const TwF* src = PassTw<B, R>::fwd();
+        for (int i = tid; i < N; i += nt) dst[offset<B>() + i] = src[i];
+        fill<Pass<B>::BP>(dst, tid, nt);
+      }
+    }
+    template <int B, class WW, int RR>
+    __device__ __forceinline__ void item(int /*n*/, int k, WW (&out)[RR]) const {
+      TwF f[RR];
+      __builtin_memcpy(f, base + offset<B>() + k * RR, sizeof(f));
+#pragma unroll
+      for (int j = 0; j < RR; ++j) {
+        if constexpr (std::is_same<WW, TwF>::value)
+          out[j] = f[j];
+        else
+          out[j] = Tw{f[j].c, f[j].c * f[j].tn};
+      }
+    }
+  };
+
+  // Both directions' twiddles for a kernel that runs forward and inverse
+  // transforms: register copies (IN_LDS false) or one LDS table of
+  // lds_floats() floats that init() fills cooperatively (a barrier must follow
+  // before the first transform).
+  template <bool IN_LDS, int D = 0>
+  struct TwSet {
+    FwdTws f;
+    InvTws i;
+    static constexpr int lds_floats() { return 0; }
+    __device__ __forceinline__ void init(TwF*, int, int, int t) {
+      f.load(t);
+      i.load(t);
+    }
+    __device__ __forceinline__ const FwdTws& fwd() const { return f; }
+    __device__ __forceinline__ const InvTws& inv() const { return i; }
+  };
+  template <int D>
+  struct TwSet<true, D> {
+    LdsTws l;
+    static constexpr int lds_floats() { return (2 * LdsTws::entries() + 3) / 4 * 4; }
+    __device__ __forceinline__ void init(TwF* dst, int tid, int nt, int) {
+      LdsTws::fill(dst, tid, nt);
+      l.base = dst;
+    }
+    __device__ __forceinline__ const LdsTws& fwd() const { return l; }
+    __device__ __forceinline__ const LdsTws& inv() const { return l; }
+  };
 
   // ---- forward ----------------------------------------------------------
   // pass 0: thread t reads elements t + T*s (coalesced across threads)
@@ -466,10 +538,13 @@ struct Row {
         v[2 * q] = L[addr<B>(r, k)];
         v[2 * q + 1] = L[addr<B>(r, k2)];
       }
-      if (k == 0)
+      if (k == 0) {
         item0_fwd<R>(v);
-      else
-        item_fwd<B, R>(v, tw[n]);
+      } else {
+        TwF w[R];
+        tw.template item<B>(n, k, w);
+        item_fwd<B, R>(v, w);
+      }
     }
   }
 
@@ -530,10 +605,13 @@ struct Row {
         v[2 * q] = src(addr<PS::BP>(rp, k), q * B);
         v[2 * q + 1] = src(addr<PS::BP>(rp, k2), q * B);
       }
-      if (k == 0)
+      if (k == 0) {
         item0_inv<R>(v);
-      else
-        item_inv<B, R>(v, tw[n]);
+      } else {
+        Tw w[R];
+        tw.template item<B>(n, k, w);
+        item_inv<B, R>(v, w);
+      }
     }
   }
 
@@ -567,10 +645,13 @@ struct Row {
       float* v = a + 2 * R * n;
 #pragma unroll
       for (int j = 0; j < 2 * R; ++j) v[j] = widen(raw[2 * R * n + j]);
-      if (k == 0)
+      if (k == 0) {
         item0_inv<R>(v);
-      else
-        item_inv<B, R>(v, tw[n]);
+      } else {
+        Tw w[R];
+        tw.template item<B>(n, k, w);
+        item_inv<B, R>(v, w);
+      }
     }
   }
 

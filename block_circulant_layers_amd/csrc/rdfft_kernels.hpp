@@ -27,7 +27,7 @@ __device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, 
   using Rw = Row<P, E>;
   using PS = typename Rw::template Pass<B>;
   __syncthreads();  // the previous pass's scatter is visible
-  Rw::template fwd_pass<B>(a, L, t, tw.template at<B>());
+  Rw::template fwd_pass<B>(a, L, t, tw);
   if constexpr (PS::BP == P && !TO_LDS) {
     Rw::template last_store<B>(a, t, st);
   } else {
@@ -47,14 +47,14 @@ __device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld, 
   auto from_lds = [L](int v, int c) { return L[v + c]; };
   if constexpr (PS::BP == P) {
     if constexpr (FROM_LDS) {
-      Rw::template inv_pass<B>(a, from_lds, t, tw.template at<B>());
+      Rw::template inv_pass<B>(a, from_lds, t, tw);
       __syncthreads();
     } else {
-      Rw::template inv_pass<B>(a, ld, t, tw.template at<B>());
+      Rw::template inv_pass<B>(a, ld, t, tw);
     }
   } else {
     inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld, tw);
-    Rw::template inv_pass<B>(a, from_lds, t, tw.template at<B>());
+    Rw::template inv_pass<B>(a, from_lds, t, tw);
     __syncthreads();  // every gather of this exchange is done
   }
   Rw::template inv_scatter<B>(a, L, t);
@@ -68,7 +68,7 @@ __device__ __forceinline__ void inv_down(float (&a)[E], float* L, int t, const T
   if constexpr (Bout > E) {
     using Rw = Row<P, E>;
     constexpr int B = Rw::pass_in_for(Bout);
-    Rw::template inv_pass<B>(a, [L](int v, int c) { return L[v + c]; }, t, tw.template at<B>());
+    Rw::template inv_pass<B>(a, [L](int v, int c) { return L[v + c]; }, t, tw);
     __syncthreads();  // every gather of this exchange is done
     Rw::template inv_scatter<B>(a, L, t);
     __syncthreads();
@@ -86,6 +86,24 @@ __device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW&
   using Rw = Row<P, E>;
   float a[E];
   Rw::fwd_pass0(a, ld, t);
+  if constexpr (P == E) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) L[s] = a[s];
+  } else {
+    Rw::fwd_pass0_scatter(a, L, t);
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw);
+  }
+}
+
+// The same from values already loaded (raw[s] = element t + T*s, widened by
+// widen): used where the loads were issued ahead of time.
+template <int P, class V, class Wd, class TW>
+__device__ __forceinline__ void row_fwd_raw_to_lds(const V (&raw)[elems_per_thread(P)], Wd widen, float* L, int t,
+                                                   const TW& tw) {
+  constexpr int E = elems_per_thread(P);
+  using Rw = Row<P, E>;
+  float a[E];
+  Rw::fwd_pass0_from(a, raw, widen);
   if constexpr (P == E) {
 #pragma unroll
     for (int s = 0; s < P; ++s) L[s] = a[s];
@@ -219,7 +237,7 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
       small_inv<P, 1>(a);
     } else {
       constexpr int BL = Rw::pass_in_for(P);
-      Rw::template inv_first_from<BL>(a, raw, widen, t, tw.template at<BL>());
+      Rw::template inv_first_from<BL>(a, raw, widen, t, tw);
     }
     const __amdgpu_buffer_rsrc_t rs = rsrc(g);
     const int64_t gn = g + gridDim.x;

@@ -106,9 +106,67 @@ int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int6
   return launch_rdfft<P, F32Io, true>(dc, q * k, s);
 }
 
+constexpr int64_t kMaxLds = 160 * 1024;
+constexpr int64_t kTargetWgs = 256;  // workgroups per launch of the token-persistent kernels
+
+// token split: about kTargetWgs workgroups over `tiles` weight tiles, tpw a multiple of tb
+int64_t tokens_per_wg(int64_t batch, int64_t tiles, int tb) {
+  int64_t gx = kTargetWgs / tiles;
+  if (gx < 1) gx = 1;
+  int64_t tpw = (batch + gx - 1) / gx;
+  return (tpw + tb - 1) / tb * tb;
+}
+
+template <int P, class Io>
+int launch_circ_product(const void* in, const float* c, void* out, int64_t batch, int64_t nin, int64_t nout, bool trans,
+                        hipStream_t s) {
+  if constexpr (P >= 64) {
+    using S = TpShape<P>;
+    if (nin <= S::CR && S::fits(static_cast<int>(nin)) && S::lds_bytes(static_cast<int>(nin)) <= kMaxLds &&
+        nout <= 0x7fffffff) {
+      const int64_t gy = (nout + S::K.to - 1) / S::K.to;
+      const int64_t tpw = tokens_per_wg(batch, gy, S::K.tb);
+      const int64_t gx = (batch + tpw - 1) / tpw;
+      if (gx > 0x7fffffff || gy > 65535) return RDFFT_ERR_SIZE;
+      const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+      const size_t lds = static_cast<size_t>(S::lds_bytes(static_cast<int>(nin)));
+      const auto* pi = static_cast<const typename Io::T*>(in);
+      auto* po = static_cast<typename Io::T*>(out);
+      if (trans)
+        circ_tp_kernel<P, true, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw);
+      else
+        circ_tp_kernel<P, false, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw);
+      return launch_status();
+    }
+  }
+  return launch_circ_mm<P, Io>(in, c, out, batch, nin, nout, trans, s);
+}
+
+template <int P, class Io>
+int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s) {
+  if constexpr (P >= 64) {
+    using S = DtpShape<P>;
+    const int64_t gy = (q + S::K.ti - 1) / S::K.ti, gz = (k + S::K.tj - 1) / S::K.tj;
+    if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
+    const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb);
+    const int64_t gx = (batch + tpw - 1) / tpw;
+    if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
+    int st = launch_fill_zero(dc, q * k * P, s);
+    if (st != RDFFT_OK) return st;
+    circ_dctp_kernel<P, Io><<<dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(S::K.nt),
+                              static_cast<size_t>(S::lds_bytes()), s>>>(
+        static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k), int(q), tpw);
+    st = launch_status();
+    if (st != RDFFT_OK) return st;
+    return launch_rdfft<P, F32Io, true>(dc, q * k, s);
+  } else {
+    return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s);
+  }
+}
+
 template <int P, class Io>
 int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, hipStream_t s) {
-  return launch_circ_mm<P, Io>(x, c, y, batch, d_in / P, d_out / P, false, s);
+  return launch_circ_product<P, Io>(x, c, y, batch, d_in / P, d_out / P, false, s);
 }
 
 template <int P, class Io>
@@ -117,10 +175,10 @@ int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* d
   const int64_t k = d_in / P, q = d_out / P;
   if (batch == 0) return dc ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
   if (dx) {
-    const int st = launch_circ_mm<P, Io>(dy, c, dx, batch, q, k, true, s);
+    const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s);
     if (st != RDFFT_OK) return st;
   }
-  if (dc) return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s);
+  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s);
   return RDFFT_OK;
 }
 

@@ -16,8 +16,14 @@ namespace rdfft {
 __host__ __device__ constexpr int elems_per_thread(int P) { return P < 16 ? P : 16; }
 // threads per workgroup of the standalone kernels: at least 256, or one whole row
 __host__ __device__ constexpr int wg_threads(int P, int E) { return (P / E) > 256 ? (P / E) : 256; }
-// resident workgroups per CU the standalone kernels are launched for
-__host__ __device__ constexpr int wg_per_cu(int P) { return P >= 1024 ? 4 : 2; }
+// resident workgroups per CU the standalone kernels are launched for (fp32
+// rows of p >= 1024: two workgroups, each looping over more groups, measured
+// faster than four; a second group of look-ahead measured slower)
+__host__ __device__ constexpr int wg_per_cu(int P, bool f32) { return P >= 1024 ? (f32 ? 2 : 4) : 2; }
+template <class Io>
+constexpr bool is_f32_io() {
+  return sizeof(typename Io::T) == 4;
+}
 
 // Forward passes with input spectra of size B and all later ones.  The last
 // pass either stores the natural packed row through st (global) or, when
@@ -138,48 +144,49 @@ __device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float s
 
 // ---------------------------------------------------------------------------
 // standalone kernels: persistent workgroups, each looping over groups of ROWS
-// rows with the next group's loads issued before the current group is
+// rows, with the next group's loads issued before the current group is
 // transformed (its values wait in registers), so loads, arithmetic and stores
 // of different groups overlap.  The twiddles depend only on the thread and
 // stay in registers across the loop.
 // ---------------------------------------------------------------------------
 template <int P, class Io>
-__global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
+__global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)),
+                                  wg_per_cu(P, is_f32_io<Io>()) *
+                                      wg_threads(P, elems_per_thread(P)) / 256)
     rdfft_fwd_kernel(typename Io::T* __restrict__ data, int64_t rows) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   constexpr int T = Rw::T;
   constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / T;
+  constexpr int SEG = cmin(T, 64) * static_cast<int>(sizeof(typename Io::T));  // bytes per row per wave access
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
   const int tid = threadIdx.x;
   const int rl = tid / T, t = tid % T;
   const int ro = rl * P;
   const int64_t ngroups = (rows + ROWS - 1) / ROWS;
+  const int64_t G = gridDim.x;
   int64_t g = blockIdx.x;
   if (g >= ngroups) return;
   auto rsrc = [data, rows](int64_t gg) {
     const int64_t r0 = gg * ROWS;
     return make_rsrc<Io>(data + r0 * P, ((rows - r0 < ROWS) ? rows - r0 : ROWS) * P);
   };
+  auto load = [=](typename Io::T(&raw)[E], int64_t gg) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(gg);
+    Rw::fwd_load0(raw, [rs, ro](int v, int c) { return Io::template braw<row_load_aux(SEG)>(rs, ro + v, c); }, t);
+  };
   typename Io::T raw[E];
-  {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(g);
-    Rw::fwd_load0(raw, [rs, ro](int v, int c) { return Io::braw(rs, ro + v, c); }, t);
-  }
+  load(raw, g);
   typename Rw::FwdTws tw;
   tw.load(t);
   float* L = lds + rl * Rw::LDS;
   while (true) {
     float a[E];
     Rw::fwd_pass0_from(a, raw, [](typename Io::T v) { return Io::widen(v); });
+    if (g + G < ngroups) load(raw, g + G);
     const __amdgpu_buffer_rsrc_t rs = rsrc(g);
-    const int64_t gn = g + gridDim.x;
-    if (gn < ngroups) {
-      const __amdgpu_buffer_rsrc_t rn = rsrc(gn);
-      Rw::fwd_load0(raw, [rn, ro](int v, int c) { return Io::braw(rn, ro + v, c); }, t);
-    }
-    auto st = [rs, ro](int v, int c, float x) { Io::bstore(rs, ro + v, c, x); };
+    auto st = [rs, ro](int v, int c, float x) { Io::template bstore<row_store_aux(SEG)>(rs, ro + v, c, x); };
     if constexpr (P == E) {
 #pragma unroll
       for (int s = 0; s < P; ++s) st(0, s, a[s]);
@@ -187,26 +194,30 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
       Rw::fwd_pass0_scatter(a, L, t);
       fwd_rest<P, E, E, false>(a, L, t, st, tw);
     }
-    g = gn;
-    if (g >= ngroups) break;
+    g += G;
+    if (g >= ngroups) return;
     if constexpr (P != E) __syncthreads();  // the last gathers are done before LDS is reused
   }
 }
 
 template <int P, class Io>
-__global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
+__global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)),
+                                  wg_per_cu(P, is_f32_io<Io>()) *
+                                      wg_threads(P, elems_per_thread(P)) / 256)
     rdfft_inv_kernel(typename Io::T* __restrict__ data, int64_t rows) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   constexpr int T = Rw::T;
   constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / T;
+  constexpr int SEG = cmin(T, 64) * static_cast<int>(sizeof(typename Io::T));  // bytes per row per wave access
   constexpr float scale = 1.0f / static_cast<float>(P);
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
   const int tid = threadIdx.x;
   const int rl = tid / T, t = tid % T;
   const int ro = rl * P;
   const int64_t ngroups = (rows + ROWS - 1) / ROWS;
+  const int64_t G = gridDim.x;
   int64_t g = blockIdx.x;
   if (g >= ngroups) return;
   auto rsrc = [data, rows](int64_t gg) {
@@ -214,8 +225,9 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
     return make_rsrc<Io>(data + r0 * P, ((rows - r0 < ROWS) ? rows - r0 : ROWS) * P);
   };
   // loads of a group: the natural packed row as the first inverse pass wants it
-  auto load = [=](typename Io::T(&raw)[E], __amdgpu_buffer_rsrc_t rs) {
-    auto ld = [rs, ro](int v, int c) { return Io::braw(rs, ro + v, c); };
+  auto load = [=](typename Io::T(&raw)[E], int64_t gg) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(gg);
+    auto ld = [rs, ro](int v, int c) { return Io::template braw<row_load_aux(SEG)>(rs, ro + v, c); };
     if constexpr (P == E) {
 #pragma unroll
       for (int s = 0; s < P; ++s) raw[s] = ld(0, s);
@@ -224,7 +236,7 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
     }
   };
   typename Io::T raw[E];
-  load(raw, rsrc(g));
+  load(raw, g);
   typename Rw::InvTws tw;
   tw.load(t);
   float* L = lds + rl * Rw::LDS;
@@ -239,10 +251,9 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
       constexpr int BL = Rw::pass_in_for(P);
       Rw::template inv_first_from<BL>(a, raw, widen, t, tw);
     }
+    if (g + G < ngroups) load(raw, g + G);
     const __amdgpu_buffer_rsrc_t rs = rsrc(g);
-    const int64_t gn = g + gridDim.x;
-    if (gn < ngroups) load(raw, rsrc(gn));
-    auto st = [rs, ro](int v, int c, float x) { Io::bstore(rs, ro + v, c, x); };
+    auto st = [rs, ro](int v, int c, float x) { Io::template bstore<row_store_aux_strided(SEG)>(rs, ro + v, c, x); };
     if constexpr (P == E) {
       constexpr int LP = ilog2(P);
 #pragma unroll
@@ -254,8 +265,8 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)))
       inv_down<P, E, BL>(a, L, t, tw);
       Rw::inv_pass0_store(a, L, t, scale, st);
     }
-    g = gn;
-    if (g >= ngroups) break;
+    g += G;
+    if (g >= ngroups) return;
     if constexpr (P != E) __syncthreads();  // the last gathers are done before LDS is reused
   }
 }

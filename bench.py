@@ -173,6 +173,30 @@ def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
     }
 
 
+def bench_copy(nbytes, steps, warmup):
+    """A plain device copy of nbytes (torch copy_, one read and one write of
+    every byte) over the same 1 GiB rotation: the practical ceiling a transform
+    of the same algorithmic bytes is compared with."""
+    n = nbytes // 4
+    nbuf = max(2, ROTATE_BYTES // nbytes)
+    bufs = [torch.zeros(n, device="cuda") for _ in range(nbuf)]
+    # buffer i is read half a rotation after it was last written: out of every cache
+    g = _replayer(lambda: [bufs[(i + nbuf // 2) % nbuf].copy_(bufs[i]) for i in range(nbuf)], False)
+    for _ in range(max(1, -(-warmup // nbuf))):
+        g()
+    reps = max(1, -(-steps // nbuf))
+    tm = Timer()
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(reps):
+        g()
+    us = tm.stop() * 1e3 / (reps * nbuf)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"us_per_copy": round(us, 3), "gbs": round(2 * nbytes / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * 2 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
+
+
 def cpu_baseline_rdfft(rows, p, seconds=10.0):
     """The fp64 oracle, unmodified, on the headline workload until ~`seconds`."""
     from oracle import rdfft_oracle as ro
@@ -373,6 +397,9 @@ def main():
                 "fwd_kernel_ms": round(e["fwd_ms"], 5),
                 "inv_kernel_ms": round(e["inv_ms"], 5),
             }
+        for mib in (8, 64):
+            log(f"extra: device copy {mib} MiB")
+            extra[f"copy_ceiling_{mib}mib"] = bench_copy(mib << 20, 1024, 128)
         for pp in (128, 512, 4096):
             log(f"extra: circulant layer D=4096 B=256 p={pp}")
             extra[f"circulant_d4096_b256_p{pp}_bf16"] = bench_circ_layer(256, 4096, pp, 256, 32)

@@ -107,19 +107,23 @@ int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int6
 }
 
 constexpr int64_t kMaxLds = 160 * 1024;
-constexpr int64_t kTargetWgs = 256;  // workgroups per launch of the token-persistent kernels
+constexpr int64_t kTargetWgs = 256;    // workgroups per launch of the token-persistent kernels
+constexpr int64_t kDctpTargetWgs = 256;  // the same for the dc kernel
 
-// token split: about kTargetWgs workgroups over `tiles` weight tiles, tpw a multiple of tb
-int64_t tokens_per_wg(int64_t batch, int64_t tiles, int tb) {
-  int64_t gx = kTargetWgs / tiles;
+// token split: about `target` workgroups over `tiles` weight tiles, tpw a multiple of tb
+int64_t tokens_per_wg(int64_t batch, int64_t tiles, int tb, int64_t target = kTargetWgs) {
+  int64_t gx = target / tiles;
   if (gx < 1) gx = 1;
   int64_t tpw = (batch + gx - 1) / gx;
   return (tpw + tb - 1) / tb * tb;
 }
 
+// y = circulant product of `in` (forward, or transposed for dx).  When the
+// token-persistent kernel runs, it also clears zero[0..nzero) and sets
+// *zeroed; otherwise zero is left alone.
 template <int P, class Io>
 int launch_circ_product(const void* in, const float* c, void* out, int64_t batch, int64_t nin, int64_t nout, bool trans,
-                        hipStream_t s) {
+                        hipStream_t s, float* zero = nullptr, int64_t nzero = 0, bool* zeroed = nullptr) {
   if constexpr (P >= 64) {
     using S = TpShape<P>;
     if (nin <= S::CR && S::fits(static_cast<int>(nin)) && S::lds_bytes(static_cast<int>(nin)) <= kMaxLds &&
@@ -132,10 +136,14 @@ int launch_circ_product(const void* in, const float* c, void* out, int64_t batch
       const size_t lds = static_cast<size_t>(S::lds_bytes(static_cast<int>(nin)));
       const auto* pi = static_cast<const typename Io::T*>(in);
       auto* po = static_cast<typename Io::T*>(out);
+      if (!zero) nzero = 0;
       if (trans)
-        circ_tp_kernel<P, true, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw);
+        circ_tp_kernel<P, true, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw, zero,
+                                                                    nzero);
       else
-        circ_tp_kernel<P, false, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw);
+        circ_tp_kernel<P, false, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw,
+                                                                     zero, nzero);
+      if (zeroed) *zeroed = nzero > 0;
       return launch_status();
     }
   }
@@ -143,15 +151,16 @@ int launch_circ_product(const void* in, const float* c, void* out, int64_t batch
 }
 
 template <int P, class Io>
-int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s) {
+int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s,
+                       bool zeroed) {
   if constexpr (P >= 64) {
     using S = DtpShape<P>;
     const int64_t gy = (q + S::K.ti - 1) / S::K.ti, gz = (k + S::K.tj - 1) / S::K.tj;
     if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
-    const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb);
+    const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb, kDctpTargetWgs);
     const int64_t gx = (batch + tpw - 1) / tpw;
     if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
-    int st = launch_fill_zero(dc, q * k * P, s);
+    int st = zeroed ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);
     if (st != RDFFT_OK) return st;
     circ_dctp_kernel<P, Io><<<dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(S::K.nt),
                               static_cast<size_t>(S::lds_bytes()), s>>>(
@@ -174,11 +183,12 @@ int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* d
                int64_t d_out, hipStream_t s) {
   const int64_t k = d_in / P, q = d_out / P;
   if (batch == 0) return dc ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
+  bool zeroed = false;  // dc cleared by the dx kernel
   if (dx) {
-    const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s);
+    const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s, dc, dc ? q * k * P : 0, &zeroed);
     if (st != RDFFT_OK) return st;
   }
-  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s);
+  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s, zeroed);
   return RDFFT_OK;
 }
 

@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 import block_circulant_layers_amd as bcl  # noqa: E402
 from block_circulant_layers_amd import synthetic as syn  # noqa: E402
 
-IO_NAME = {"f32": "F32Io", "bf16": "Bf16Io"}
+IO_NAME = {"f32": "F32Io", "bf16": "Bf16Io", "f16": "F16Io"}
 METRIC = "rdFFT GB/s + % HBM peak (p=512,4096); circulant fwd+bwd tokens/s"
 HBM_PEAK_GBS = 8000.0
 VALU_FP32_PEAK_TFS = 157.3
@@ -126,7 +126,7 @@ def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
     nbuf forwards, then all nbuf inverses (each buffer gets forward then
     inverse, as in a step).  Events around the forward graph give the forward
     kernel's mean launch duration."""
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     eb = 4 if dtype == "f32" else 2
     nbytes = rows * p * eb
     nbuf = max(2, ROTATE_BYTES // nbytes)
@@ -173,6 +173,33 @@ def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
     }
 
 
+def bench_spectrum(rows, p, steps, warmup):
+    """rdfft_unpack then rdfft_pack over a rotating set: GB/s of each (bytes =
+    packed rows read or written + complex bins written or read)."""
+    nbytes = rows * p * 4
+    nbuf = max(2, ROTATE_BYTES // (2 * nbytes))
+    zs = [syn.torch_normal((rows, p), syn.WL_TEST, syn.T_X, i) for i in range(nbuf)]
+    ss = [torch.empty(rows, p // 2 + 1, 2, device="cuda") for _ in range(nbuf)]
+    out = {}
+    for name, fn in (("unpack", lambda: [bcl.rdfft_unpack(z, s) for z, s in zip(zs, ss)]),
+                     ("pack", lambda: [bcl.rdfft_pack(s, z) for z, s in zip(zs, ss)])):
+        g = _replayer(fn, False)
+        for _ in range(max(1, -(-warmup // nbuf))):
+            g()
+        reps = max(1, -(-steps // nbuf))
+        tm = Timer()
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(reps):
+            g()
+        us = tm.stop() * 1e3 / (reps * nbuf)
+        moved = nbytes + rows * (p + 2) * 4
+        out[name] = {"us": round(us, 3), "gbs": round(moved / us / 1e3, 1)}
+    del zs, ss
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_copy(nbytes, steps, warmup):
     """A plain device copy of nbytes (torch copy_, one read and one write of
     every byte) over the same 1 GiB rotation: the practical ceiling a transform
@@ -195,6 +222,29 @@ def bench_copy(nbytes, steps, warmup):
     torch.cuda.empty_cache()
     return {"us_per_copy": round(us, 3), "gbs": round(2 * nbytes / us / 1e3, 1),
             "pct_hbm_peak": round(100 * 2 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
+
+
+def bench_layer_memory(batch, d, p):
+    """Peak device memory of one BlockCirculantLinear forward + backward in
+    fp32, counted from an empty allocator: parameters c, their gradient, x,
+    y, dy and dx (the quantities a single-layer peak-memory figure holds),
+    and what the step needed beyond those tensors (workspace)."""
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    layer = bcl.BlockCirculantLinear(d, d, p, device="cuda")
+    x = syn.torch_normal((batch, d), syn.WL_TEST, syn.T_X, 99).requires_grad_(True)
+    dy = syn.torch_normal((batch, d), syn.WL_TEST, syn.T_DY, 99)
+    y = layer(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    held = sum(-(-t.numel() * t.element_size() // 512) * 512 for t in (layer.c, layer.c.grad, x, x.grad, y, dy))
+    out = {"peak_mib": round(peak / 2**20, 4), "workspace_bytes": int(peak - held)}
+    del layer, x, dy, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline_rdfft(rows, p, seconds=10.0):
@@ -316,7 +366,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rows", type=int, default=4096, help="transform rows of the timed workload")
     ap.add_argument("--p", type=int, default=512, help="row length of the timed workload")
-    ap.add_argument("--dtype", choices=("f32", "bf16"), default="f32", help="storage type of the timed workload")
+    ap.add_argument("--dtype", choices=("f32", "bf16", "f16"), default="f32", help="storage type of the timed workload")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed transforms directly instead of from HIP graphs (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -397,12 +447,31 @@ def main():
                 "fwd_kernel_ms": round(e["fwd_ms"], 5),
                 "inv_kernel_ms": round(e["inv_ms"], 5),
             }
+        for (r, pp, dt) in ((4096, 4096, "f16"),):
+            log(f"extra: rdfft {r}x{pp} {dt}")
+            e = bench_rdfft(r, pp, dt, max(256, args.steps // 4), max(32, args.warmup // 4), syn.WL_RDFFT_LARGE)
+            ach = e["bytes_per_launch"] / (e["fwd_ms"] * 1e-3) / 1e9
+            extra[f"rdfft_{r}x{pp}_{dt}"] = {
+                "gbs_fwd_plus_inv": round(e["gbs"], 1),
+                "pct_hbm_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 2),
+                "fwd_kernel_gbs": round(ach, 1),
+                "fwd_kernel_ms": round(e["fwd_ms"], 5),
+                "inv_kernel_ms": round(e["inv_ms"], 5),
+            }
+        log("extra: unpack / pack 4096x512 f32")
+        extra["spectrum_unpack_pack_4096x512_f32"] = bench_spectrum(4096, 512, 1024, 128)
         for mib in (8, 64):
             log(f"extra: device copy {mib} MiB")
             extra[f"copy_ceiling_{mib}mib"] = bench_copy(mib << 20, 1024, 128)
         for pp in (128, 512, 4096):
             log(f"extra: circulant layer D=4096 B=256 p={pp}")
             extra[f"circulant_d4096_b256_p{pp}_bf16"] = bench_circ_layer(256, 4096, pp, 256, 32)
+        log("extra: single-layer peak memory")
+        mem = {}
+        for (b, d, pp) in ((1, 4096, 128), (1, 4096, 512), (1, 4096, 1024), (1, 4096, 4096), (256, 4096, 128),
+                           (256, 4096, 512), (256, 4096, 1024), (256, 4096, 4096), (1, 1024, 1024)):
+            mem[f"d{d}_b{b}_p{pp}"] = bench_layer_memory(b, d, pp)
+        extra["layer_peak_memory_f32"] = mem
         log("extra: 128 circulant adapters 4096x4096 p=1024, 2048 tokens")
         extra["circulant_128_adapters_d4096_p1024_b2048_bf16"] = bench_circ_adapters(10, 2)
         out["extra"] = extra

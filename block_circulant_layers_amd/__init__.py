@@ -7,6 +7,7 @@ Python binding.  Build with ``python -m block_circulant_layers_amd.build``.
 
 from .binding import (  # noqa: F401
     RDFFT_BF16,
+    RDFFT_F16,
     RDFFT_F32,
     RdfftError,
     circulant_bwd,
@@ -15,4 +16,7 @@ from .binding import (  # noqa: F401
     lib_path,
     rdfft_forward,
     rdfft_inverse,
+    rdfft_pack,
+    rdfft_unpack,
 )
+from .layer import BlockCirculantFunction, BlockCirculantLinear  # noqa: F401

@@ -25,10 +25,14 @@ __all__ = [
     "circulant_bwd",
     "RDFFT_F32",
     "RDFFT_BF16",
+    "RDFFT_F16",
+    "rdfft_unpack",
+    "rdfft_pack",
 ]
 
 RDFFT_F32 = 0
 RDFFT_BF16 = 1
+RDFFT_F16 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -43,6 +47,8 @@ SIGNATURES = {
     "rdfft_inverse": (ctypes.c_int, [_VP, _I64, _I64, ctypes.c_int, _VP]),
     "circulant_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "circulant_bwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "rdfft_unpack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
+    "rdfft_pack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
 }
 
 
@@ -81,7 +87,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return RDFFT_F32
     if t.dtype == torch.bfloat16:
         return RDFFT_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return RDFFT_F16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32, bfloat16 or float16")
 
 
 def _check_gpu(*ts: torch.Tensor) -> None:
@@ -166,3 +174,30 @@ def circulant_bwd(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: torch.
           dx.data_ptr() if dx is not None else None, dc.data_ptr() if dc is not None else None,
           batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
     return dx, dc
+
+
+def rdfft_unpack(packed: torch.Tensor, spec: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Explicit complex bins of packed spectra: returns float32 (..., p/2 + 1, 2)
+    holding (Re, Im) of bins 0..p/2 (allocated if None)."""
+    _check_gpu(packed)
+    p = packed.shape[-1] if packed.dim() else 0
+    rows = packed.numel() // p if p else 0
+    if spec is None:
+        spec = torch.empty(*packed.shape[:-1], p // 2 + 1, 2, dtype=torch.float32, device=packed.device)
+    _check_gpu(spec)
+    if spec.dtype != torch.float32 or spec.numel() != rows * (p + 2):
+        raise ValueError("spec must be float32 of shape (..., p/2 + 1, 2)")
+    _call("rdfft_unpack", packed.data_ptr(), spec.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
+    return spec
+
+
+def rdfft_pack(spec: torch.Tensor, packed: torch.Tensor, stream=None) -> torch.Tensor:
+    """Write the packed form of complex bins spec (float32 (..., p/2 + 1, 2)) into
+    ``packed`` (..., p) of its own dtype; Im of bins 0 and p/2 is not read."""
+    _check_gpu(spec, packed)
+    p = packed.shape[-1] if packed.dim() else 0
+    rows = packed.numel() // p if p else 0
+    if spec.dtype != torch.float32 or spec.numel() != rows * (p + 2):
+        raise ValueError("spec must be float32 of shape (..., p/2 + 1, 2)")
+    _call("rdfft_pack", spec.data_ptr(), packed.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
+    return packed

@@ -316,12 +316,21 @@ struct F32Io {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff * 4, soff * 4, AUX);
   }
 };
-struct Bf16Io {
-  using T = uint16_t;
+// 16-bit storage (bfloat16 or IEEE half): rows widened to fp32 on load and
+// rounded to nearest even once on store.
+struct Bf16Conv {
   static __device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
-  static __device__ __forceinline__ uint16_t narrow(float v) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
-  }
+  static __device__ __forceinline__ uint16_t narrow(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+};
+struct F16Conv {
+  static __device__ __forceinline__ float widen(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
+  static __device__ __forceinline__ uint16_t narrow(float v) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v)); }
+};
+template <class Conv>
+struct Io16 {
+  using T = uint16_t;
+  static __device__ __forceinline__ float widen(uint16_t h) { return Conv::widen(h); }
+  static __device__ __forceinline__ uint16_t narrow(float v) { return Conv::narrow(v); }
   template <int AUX = kAuxDefault>
   static __device__ __forceinline__ uint16_t braw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff * 2, soff * 2, AUX);
@@ -333,6 +342,8 @@ struct Bf16Io {
     __builtin_amdgcn_raw_buffer_store_b16(narrow(v), r, voff * 2, soff * 2, AUX);
   }
 };
+struct Bf16Io : Io16<Bf16Conv> {};
+struct F16Io : Io16<F16Conv> {};
 
 template <class Io>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const typename Io::T* base, int64_t elems) {

@@ -5,6 +5,7 @@
 #include "rdfft_kernels.hpp"
 #include "circulant_kernels.hpp"
 #include "rdfft_validate.hpp"
+#include "spectrum_kernels.hpp"
 
 namespace rdfft {
 namespace {
@@ -225,13 +226,47 @@ int circ_bwd_dispatch(const void* x, const float* c, const void* dy, void* dx, f
 #undef CALL
 }
 
+// call f(Io{}) with the storage type of dtype (validated before)
+template <class F>
+int by_dtype(int dtype, F f) {
+  switch (dtype) {
+    case RDFFT_BF16: return f(Bf16Io{});
+    case RDFFT_F16: return f(F16Io{});
+    default: return f(F32Io{});
+  }
+}
+
 template <bool INV>
 int rdfft_entry(void* data, int64_t rows, int64_t p, int dtype, void* stream) {
   const int st = check_rdfft(data, rows, p, dtype);
   if (st != RDFFT_OK || rows == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == RDFFT_BF16 ? dispatch_rdfft<Bf16Io, INV>(data, rows, p, s)
-                             : dispatch_rdfft<F32Io, INV>(data, rows, p, s);
+  return by_dtype(dtype, [&](auto io) { return dispatch_rdfft<decltype(io), INV>(data, rows, p, s); });
+}
+
+// grid of the element-wise spectrum kernels: grid-stride over total elements
+unsigned elementwise_grid(int64_t total) {
+  const int64_t cap = static_cast<int64_t>(device_cus()) * 16;
+  const int64_t want = (total + 255) / 256;
+  return static_cast<unsigned>(want < cap ? want : cap);
+}
+
+template <bool PACK>
+int spectrum_entry(const void* packed, const float* spec, int64_t rows, int64_t p, int dtype, void* stream) {
+  const int st = check_spectrum(packed, spec, rows, p, dtype);
+  if (st != RDFFT_OK || rows == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int lp = ilog2(static_cast<int>(p));
+  const unsigned grid = elementwise_grid(rows * p);
+  return by_dtype(dtype, [&](auto io) {
+    using Io = decltype(io);
+    auto* z = static_cast<typename Io::T*>(const_cast<void*>(packed));
+    if (PACK)
+      pack_kernel<Io><<<dim3(grid), dim3(256), 0, s>>>(spec, z, rows, lp);
+    else
+      unpack_kernel<Io><<<dim3(grid), dim3(256), 0, s>>>(z, const_cast<float*>(spec), rows, lp);
+    return launch_status();
+  });
 }
 
 }  // namespace
@@ -247,7 +282,7 @@ const char* rdfft_status_string(int status) {
     case RDFFT_ERR_NULL: return "null pointer";
     case RDFFT_ERR_SIZE: return "unsupported size (p must be a power of two in [2, 4096]; counts >= 0)";
     case RDFFT_ERR_SHAPE: return "d_in and d_out must be positive multiples of p";
-    case RDFFT_ERR_DTYPE: return "unknown dtype";
+    case RDFFT_ERR_DTYPE: return "unknown dtype (RDFFT_F32, RDFFT_BF16 or RDFFT_F16)";
     case RDFFT_ERR_ALIGN: return "pointer not 16-byte aligned";
     case RDFFT_ERR_ALIAS: return "output buffer overlaps another buffer";
     case RDFFT_ERR_LAUNCH: return "kernel launch failed";
@@ -268,8 +303,9 @@ int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t
   const int st = rdfft::check_circulant_fwd(x, c, y, batch, d_in, d_out, p, dtype);
   if (st != RDFFT_OK || batch == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == RDFFT_BF16 ? rdfft::circ_fwd_dispatch<rdfft::Bf16Io>(x, c, y, batch, d_in, d_out, p, s)
-                             : rdfft::circ_fwd_dispatch<rdfft::F32Io>(x, c, y, batch, d_in, d_out, p, s);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_fwd_dispatch<decltype(io)>(x, c, y, batch, d_in, d_out, p, s);
+  });
 }
 
 int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
@@ -277,8 +313,17 @@ int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float
   const int st = rdfft::check_circulant_bwd(x, c, dy, dx, dc, batch, d_in, d_out, p, dtype);
   if (st != RDFFT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == RDFFT_BF16 ? rdfft::circ_bwd_dispatch<rdfft::Bf16Io>(x, c, dy, dx, dc, batch, d_in, d_out, p, s)
-                             : rdfft::circ_bwd_dispatch<rdfft::F32Io>(x, c, dy, dx, dc, batch, d_in, d_out, p, s);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, s);
+  });
+}
+
+int rdfft_unpack(const void* packed, float* spec, int64_t rows, int64_t p, int dtype, void* stream) {
+  return rdfft::spectrum_entry<false>(packed, spec, rows, p, dtype, stream);
+}
+
+int rdfft_pack(const float* spec, void* packed, int64_t rows, int64_t p, int dtype, void* stream) {
+  return rdfft::spectrum_entry<true>(packed, spec, rows, p, dtype, stream);
 }
 
 }  // extern "C"

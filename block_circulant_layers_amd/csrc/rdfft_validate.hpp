@@ -11,8 +11,8 @@
 namespace rdfft {
 
 inline bool valid_len(int64_t p) { return p >= 2 && p <= 4096 && (p & (p - 1)) == 0; }
-inline bool valid_dtype(int dtype) { return dtype == RDFFT_F32 || dtype == RDFFT_BF16; }
-inline int64_t dtype_bytes(int dtype) { return dtype == RDFFT_BF16 ? 2 : 4; }
+inline bool valid_dtype(int dtype) { return dtype == RDFFT_F32 || dtype == RDFFT_BF16 || dtype == RDFFT_F16; }
+inline int64_t dtype_bytes(int dtype) { return dtype == RDFFT_F32 ? 4 : 2; }
 inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // half-open byte ranges [a, a+na) and [b, b+nb) overlap
@@ -31,6 +31,17 @@ inline int check_rdfft(const void* data, int64_t rows, int64_t p, int dtype) {
   if (rows == 0) return RDFFT_OK;
   if (data == nullptr) return RDFFT_ERR_NULL;
   if (!aligned16(data)) return RDFFT_ERR_ALIGN;
+  return RDFFT_OK;
+}
+
+// packed rows [rows, p] of dtype and their complex bins [rows, p/2 + 1, 2] float
+inline int check_spectrum(const void* packed, const float* spec, int64_t rows, int64_t p, int dtype) {
+  if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;
+  if (!valid_len(p) || rows < 0 || rows > kMaxElems / (p + 2)) return RDFFT_ERR_SIZE;
+  if (rows == 0) return RDFFT_OK;
+  if (packed == nullptr || spec == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(spec)) return RDFFT_ERR_ALIGN;
+  if (overlaps(packed, rows * p * dtype_bytes(dtype), spec, rows * (p + 2) * 4)) return RDFFT_ERR_ALIAS;
   return RDFFT_OK;
 }
 

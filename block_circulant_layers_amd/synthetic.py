@@ -36,10 +36,10 @@ def normal(shape, workload: int, tensor: int, index: int = 0, scale: float = 1.0
 
 
 def cast_like_device(a: np.ndarray, dtype: str):
-    """Round a float64 array to the device dtype ("f32" or "bf16").
+    """Round a float64 array to the device dtype ("f32", "bf16" or "f16").
 
     Returns (torch CPU tensor in that dtype, float64 numpy array of the rounded
-    values).  bf16 rounding is torch's round-to-nearest-even.
+    values).  16-bit rounding is torch's round-to-nearest-even.
     """
     import torch
 
@@ -48,6 +48,8 @@ def cast_like_device(a: np.ndarray, dtype: str):
         tt = t.to(torch.float32)
     elif dtype == "bf16":
         tt = t.to(torch.bfloat16)
+    elif dtype == "f16":
+        tt = t.to(torch.float16)
     else:
         raise ValueError(f"unknown dtype {dtype!r}")
     return tt, tt.to(torch.float64).numpy()

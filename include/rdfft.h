@@ -24,10 +24,11 @@
  *     error the call returns a nonzero status and neither reads nor writes
  *     device memory.  Size 0 (rows or batch) is a no-op returning RDFFT_OK;
  *     pointers are not checked then.
- *   - `dtype` selects the storage type of the row data (data, x, y, dy, dx):
- *     RDFFT_F32 (float) or RDFFT_BF16 (bfloat16).  All arithmetic is fp32;
- *     bf16 results are rounded to nearest even once, on store.  The
- *     circulant parameters c and their gradient dc are always float.
+ *   - `dtype` selects the storage type of the row data (data, x, y, dy, dx,
+ *     packed): RDFFT_F32 (float), RDFFT_BF16 (bfloat16) or RDFFT_F16 (IEEE
+ *     half).  All arithmetic is fp32; 16-bit results are rounded to nearest
+ *     even once, on store.  The circulant parameters c, their gradient dc and
+ *     explicit complex spectra are always float.
  *   - Supported row / block lengths: p = 2, 4, 8, ..., 4096.
  *   - Non-finite inputs are propagated, not checked.
  */
@@ -40,18 +41,19 @@
 extern "C" {
 #endif
 
-#define RDFFT_ABI_VERSION 1
+#define RDFFT_ABI_VERSION 2
 
 /* storage types */
 #define RDFFT_F32 0
 #define RDFFT_BF16 1
+#define RDFFT_F16 2
 
 /* status codes */
 #define RDFFT_OK 0
 #define RDFFT_ERR_NULL 1   /* a required pointer is NULL */
 #define RDFFT_ERR_SIZE 2   /* p not a power of two in [2, 4096], or a negative / too large count */
 #define RDFFT_ERR_SHAPE 3  /* d_in or d_out not a positive multiple of p */
-#define RDFFT_ERR_DTYPE 4  /* dtype not RDFFT_F32 / RDFFT_BF16 */
+#define RDFFT_ERR_DTYPE 4  /* dtype not RDFFT_F32 / RDFFT_BF16 / RDFFT_F16 */
 #define RDFFT_ERR_ALIGN 5  /* a pointer is not 16-byte aligned */
 #define RDFFT_ERR_ALIAS 6  /* an output buffer overlaps another buffer of the call */
 #define RDFFT_ERR_LAUNCH 7 /* the HIP runtime refused a kernel launch */
@@ -116,6 +118,26 @@ int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t
  */
 int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
                   int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
+
+/*
+ * rdfft_unpack -- packed spectra to explicit complex bins (the packed layout
+ * above, Paper-Notes page "Squeeze", read out).
+ *   packed [rows, p]          dtype, read only (e.g. the output of rdfft_forward)
+ *   spec   [rows, p/2 + 1, 2] float, written: (Re y_f, Im y_f) for f = 0..p/2,
+ *                             with Im y_0 = Im y_{p/2} = 0.  Must not overlap packed.
+ * Exact (values are only moved, and widened for 16-bit dtypes).
+ */
+int rdfft_unpack(const void* packed, float* spec, int64_t rows, int64_t p, int dtype, void* stream);
+
+/*
+ * rdfft_pack -- explicit complex bins to packed spectra (inverse of rdfft_unpack).
+ *   spec   [rows, p/2 + 1, 2] float, read only.  Im of bins 0 and p/2 is not
+ *                             read (the spectrum of a real row has it zero).
+ *   packed [rows, p]          dtype, written (16-bit dtypes: rounded to nearest
+ *                             even); a valid input of rdfft_inverse.  Must not
+ *                             overlap spec.
+ */
+int rdfft_pack(const float* spec, void* packed, int64_t rows, int64_t p, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = _header_functions()
     assert set(names) == {"rdfft_abi_version", "rdfft_status_string", "rdfft_forward", "rdfft_inverse",
-                          "circulant_fwd", "circulant_bwd"}
+                          "circulant_fwd", "circulant_bwd", "rdfft_unpack", "rdfft_pack"}
     for n in names:
         assert hasattr(L, n), n
     # the binding's signature table covers exactly the header
@@ -58,7 +58,7 @@ D = _header_defines()
 OK, NULL, SIZE, SHAPE, DTYPE, ALIGN, ALIAS = (D["RDFFT_OK"], D["RDFFT_ERR_NULL"], D["RDFFT_ERR_SIZE"],
                                               D["RDFFT_ERR_SHAPE"], D["RDFFT_ERR_DTYPE"], D["RDFFT_ERR_ALIGN"],
                                               D["RDFFT_ERR_ALIAS"])
-F32, BF16 = D["RDFFT_F32"], D["RDFFT_BF16"]
+F32, BF16, F16 = D["RDFFT_F32"], D["RDFFT_BF16"], D["RDFFT_F16"]
 A = ctypes.c_void_p(0x100000)  # aligned fake device addresses, never dereferenced
 B_ = ctypes.c_void_p(0x200000)
 C_ = ctypes.c_void_p(0x300000)
@@ -74,8 +74,9 @@ def test_rdfft_validation(L, fn):
         assert f(A, 4, p, F32, None) == SIZE, p
     assert f(A, -1, 512, F32, None) == SIZE
     assert f(A, 1 << 40, 4096, F32, None) == SIZE  # element count too large
-    assert f(A, 4, 512, 2, None) == DTYPE
+    assert f(A, 4, 512, 3, None) == DTYPE
     assert f(A, 4, 512, -1, None) == DTYPE
+    assert f(None, 4, 512, F16, None) == NULL
     assert f(ctypes.c_void_p(0x100004), 4, 512, F32, None) == ALIGN
     assert f(ctypes.c_void_p(0x100008), 4, 512, BF16, None) == ALIGN
 
@@ -115,6 +116,24 @@ def test_circulant_bwd_validation(L):
     assert f(A, C_, B_, ctypes.c_void_p(0x200000 + 64), DC, 2, 64, 64, 16, F32, None) == ALIAS
     assert f(A, C_, B_, DX, ctypes.c_void_p(0x300000 + 16), 2, 64, 64, 16, F32, None) == ALIAS
     assert f(A, C_, B_, None, ctypes.c_void_p(0x100000), 2, 64, 64, 16, F32, None) == ALIAS
+
+
+@pytest.mark.parametrize("fn", ["rdfft_unpack", "rdfft_pack"])
+def test_spectrum_validation(L, fn):
+    f = getattr(L, fn)
+    # argument order: (source, destination, ...) -- packed then spec for unpack, spec then packed for pack
+    assert f(A, B_, 0, 512, F32, None) == OK  # empty: no-op
+    assert f(None, B_, 4, 512, F32, None) == NULL
+    assert f(A, None, 4, 512, BF16, None) == NULL
+    for p in (0, 1, 3, 8192):
+        assert f(A, B_, 4, p, F32, None) == SIZE, p
+    assert f(A, B_, -2, 512, F32, None) == SIZE
+    assert f(A, B_, 4, 512, 7, None) == DTYPE
+    assert f(ctypes.c_void_p(0x100008), B_, 4, 512, F16, None) == ALIGN
+    assert f(A, ctypes.c_void_p(0x200004), 4, 512, F32, None) == ALIGN
+    # 4 rows of 512 floats = 8 KiB packed; 4 x 257 x 8 B spectra
+    assert f(A, ctypes.c_void_p(0x100000 + 4096), 4, 512, F32, None) == ALIAS
+    assert f(ctypes.c_void_p(0x200000 + 8176), B_, 4, 512, F32, None) == ALIAS
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,99 @@
+"""GPU tests of the autograd layer (BlockCirculantLinear) on the C ABI.
+
+Gradients through torch.autograd are compared with the fp64 oracle (per row,
+normwise relative error, the same gates as the kernel parity tests), and the
+peak allocation of a forward + backward is checked to be exactly the layer's
+outputs: no workspace.
+"""
+
+import pytest
+import torch
+
+import block_circulant_layers_amd as bcl
+from block_circulant_layers_amd import synthetic as syn
+from oracle import circulant_oracle as co
+from tests.gpu_util import TOL, TORCH_DT, device_input, row_relerr, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_with(c: torch.Tensor) -> bcl.BlockCirculantLinear:
+    q, k, p = c.shape
+    layer = bcl.BlockCirculantLinear(k * p, q * p, p, device="cuda:0")
+    with torch.no_grad():
+        layer.c.copy_(c)
+    return layer
+
+
+@pytest.mark.parametrize("batch,d_in,d_out,p,dtype,dense", [
+    (3, 64, 64, 16, "f32", True),
+    (5, 96, 160, 32, "bf16", True),
+    (7, 1024, 512, 128, "f32", False),
+    (4, 2048, 4096, 1024, "bf16", False),
+])
+def test_autograd_matches_oracle(batch, d_in, d_out, p, dtype, dense):
+    q, k = d_out // p, d_in // p
+    print(f"layer autograd B={batch} d_in={d_in} d_out={d_out} p={p} {dtype}", flush=True)
+    x, xr = device_input((batch, d_in), syn.WL_TEST, syn.T_X, 11, dtype=dtype)
+    c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, 11, scale=1 / d_in**0.5)
+    dy, dyr = device_input((batch, d_out), syn.WL_TEST, syn.T_DY, 11, dtype=dtype)
+    layer = _layer_with(c)
+    x.requires_grad_(True)
+    y = layer(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    if dense:
+        yo = co.circulant_forward_dense(xr, cr)
+        dxo, dco = co.circulant_backward_dense(xr, cr, dyr)
+    else:
+        yo = co.circulant_forward_fft(xr, cr)
+        dxo, dco = co.circulant_backward_fft(xr, cr, dyr)
+    assert y.dtype == TORCH_DT[dtype] and x.grad.dtype == TORCH_DT[dtype] and layer.c.grad.dtype == torch.float32
+    assert row_relerr(to_f64(y), yo) <= TOL[dtype]
+    assert row_relerr(to_f64(x.grad), dxo) <= TOL[dtype]
+    assert row_relerr(to_f64(layer.c.grad).reshape(q * k, p), dco.reshape(q * k, p)) <= TOL["f32"]
+
+
+def test_grad_accumulates_and_partial_needs():
+    x, _ = device_input((4, 256), syn.WL_TEST, syn.T_X, 12)
+    c, _ = device_input((2, 4, 64), syn.WL_TEST, syn.T_C, 12, scale=1 / 16)
+    dy, _ = device_input((4, 128), syn.WL_TEST, syn.T_DY, 12)
+    layer = _layer_with(c)
+    layer(x).backward(dy)
+    g1 = layer.c.grad.clone()
+    layer(x).backward(dy)  # autograd adds the second dc into .grad
+    torch.cuda.synchronize()
+    assert torch.allclose(layer.c.grad, 2 * g1, rtol=1e-6, atol=1e-6)
+    # x needs a gradient, c does not: the backward computes dx only
+    layer.c.requires_grad_(False)
+    x.requires_grad_(True)
+    layer(x).backward(dy)
+    dx_ref, _ = bcl.circulant_bwd(x.detach(), c, dy, need_dc=False)
+    torch.cuda.synchronize()
+    assert torch.equal(x.grad, dx_ref)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    # the caching allocator rounds every block up to 512 bytes
+    return -(-t.numel() * t.element_size() // 512) * 512
+
+
+@pytest.mark.parametrize("batch,d,p,dtype", [(256, 4096, 128, "bf16"), (256, 4096, 512, "bf16"),
+                                             (256, 4096, 4096, "bf16"), (2048, 4096, 1024, "bf16"),
+                                             (1, 4096, 128, "f32")])
+def test_zero_workspace(batch, d, p, dtype):
+    """Peak allocation of forward + backward = y + dx + dc exactly."""
+    print(f"layer workspace B={batch} D={d} p={p} {dtype}", flush=True)
+    x, _ = device_input((batch, d), syn.WL_TEST, syn.T_X, 13, dtype=dtype)
+    c, _ = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 13, scale=1 / d**0.5)
+    dy, _ = device_input((batch, d), syn.WL_TEST, syn.T_DY, 13, dtype=dtype)
+    layer = _layer_with(c)
+    x.requires_grad_(True)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    y = layer(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - before
+    assert peak == _nbytes(y) + _nbytes(x.grad) + _nbytes(layer.c.grad), peak

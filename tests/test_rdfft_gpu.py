@@ -2,7 +2,8 @@
 
 Every case feeds the HIP path (through the C ABI) and the oracle the same
 seeded values and compares every row: normwise relative error per row, max
-over rows, <= 1e-5 for fp32 storage and <= 2e-2 for bf16 storage.
+over rows, <= 1e-5 for fp32 storage, <= 2e-2 for bf16 storage and <= 1e-3
+for fp16 storage.
 """
 
 import numpy as np
@@ -39,7 +40,7 @@ def _check_fwd_inv(rows, p, dtype, workload=syn.WL_TEST, index=0):
     return err_f, err_i
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("p", ALL_P)
 def test_parity_all_lengths(p, dtype):
     # several workgroups plus a ragged tail

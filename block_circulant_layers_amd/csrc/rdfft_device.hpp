@@ -170,6 +170,11 @@ RDFFT_PASS_TW(128, 4)
 RDFFT_PASS_TW(128, 8)
 RDFFT_PASS_TW(1024, 2)
 RDFFT_PASS_TW(1024, 4)
+RDFFT_PASS_TW(1024, 8)
+RDFFT_PASS_TW(8192, 2)
+RDFFT_PASS_TW(8192, 4)
+RDFFT_PASS_TW(32, 16)
+RDFFT_PASS_TW(512, 16)
 #undef RDFFT_PASS_TW
 
 // the R-1 twiddles of an item, read as R/2 aligned 16-byte loads
@@ -370,7 +375,7 @@ __host__ __device__ constexpr bool class_fast(int P, int B) { return B == 128 &&
 // ---------------------------------------------------------------------------
 template <int P, int E>
 struct Row {
-  static_assert((P & (P - 1)) == 0 && P >= 2 && P <= 4096, "P must be a power of two in [2, 4096]");
+  static_assert((P & (P - 1)) == 0 && P >= 2 && P <= 32768, "P must be a power of two in [2, 32768]");
   static_assert(E <= P && (E & (E - 1)) == 0 && E >= 2, "E must be a power of two <= P");
   static constexpr int T = P / E;
 
@@ -486,6 +491,19 @@ struct Row {
         else
           out[j] = Tw{f[j].c, f[j].c * f[j].tn};
       }
+    }
+  };
+
+  // Twiddle provider reading each item's twiddles from the per-pass tables
+  // when the pass runs (kernels with too many passes or threads to keep them
+  // in registers).
+  struct GlobalTws {
+    template <int B, class WW, int RR>
+    __device__ __forceinline__ void item(int /*n*/, int k, WW (&out)[RR]) const {
+      if constexpr (std::is_same<WW, TwF>::value)
+        load_item_tw(PassTw<B, RR>::fwd(), k, out);
+      else
+        load_item_tw(PassTw<B, RR>::inv(), k, out);
     }
   };
 

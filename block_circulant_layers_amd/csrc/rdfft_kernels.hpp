@@ -287,4 +287,54 @@ __global__ void __launch_bounds__(wg_threads(P, elems_per_thread(P)),
   }
 }
 
+// ---------------------------------------------------------------------------
+// rows longer than 4096 (up to 32768, fp32 32768 = 128 KB, in one CU's LDS):
+// one workgroup per row of P/E threads (E = 16, and 32 at 32768 to stay
+// within 1024 threads), the row in dynamic LDS between passes, each pass's
+// twiddles read from the per-pass tables as it runs.  The row is read and
+// written once, like the standalone kernels above.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int long_elems(int P) { return P >= 32768 ? 32 : 16; }
+constexpr int kMaxLongP = 32768;
+
+template <int P, class Io>
+__global__ void __launch_bounds__(P / long_elems(P)) rdfft_fwd_long_kernel(typename Io::T* __restrict__ data) {
+  constexpr int E = long_elems(P);
+  using Rw = Row<P, E>;
+  constexpr int T = Rw::T;
+  constexpr int SEG = 64 * static_cast<int>(sizeof(typename Io::T));
+  extern __shared__ float lds[];
+  const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + static_cast<int64_t>(blockIdx.x) * P, P);
+  const typename Rw::GlobalTws tw;
+  float a[E];
+  Rw::fwd_pass0(a, [rs](int v, int c) { return Io::widen(Io::template braw<row_load_aux(SEG)>(rs, v, c)); }, t);
+  Rw::fwd_pass0_scatter(a, lds, t);
+  auto st = [rs](int v, int c, float x) { Io::template bstore<row_store_aux(SEG)>(rs, v, c, x); };
+  if constexpr (fwd_staged_store(P, is_f32_io<Io>())) {
+    fwd_rest<P, E, E, true>(a, lds, t, st, tw);
+    __syncthreads();  // the row is in lds[0..P) in natural packed order
+#pragma unroll
+    for (int s = 0; s < E; ++s) Io::template bstore<row_store_aux_strided(SEG)>(rs, t, T * s, lds[t + T * s]);
+  } else {
+    fwd_rest<P, E, E, false>(a, lds, t, st, tw);
+  }
+}
+
+template <int P, class Io>
+__global__ void __launch_bounds__(P / long_elems(P)) rdfft_inv_long_kernel(typename Io::T* __restrict__ data) {
+  constexpr int E = long_elems(P);
+  using Rw = Row<P, E>;
+  constexpr int SEG = 64 * static_cast<int>(sizeof(typename Io::T));
+  extern __shared__ float lds[];
+  const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + static_cast<int64_t>(blockIdx.x) * P, P);
+  const typename Rw::GlobalTws tw;
+  float a[E];
+  auto ld = [rs](int v, int c) { return Io::widen(Io::template braw<row_load_aux(SEG)>(rs, v, c)); };
+  inv_rest<P, E, E, false>(a, lds, t, ld, tw);
+  auto st = [rs](int v, int c, float x) { Io::template bstore<row_store_aux_strided(SEG)>(rs, v, c, x); };
+  Rw::inv_pass0_store(a, lds, t, 1.0f / static_cast<float>(P), st);
+}
+
 }  // namespace rdfft

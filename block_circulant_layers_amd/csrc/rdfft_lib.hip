@@ -42,6 +42,19 @@ int launch_rdfft(void* data, int64_t rows, hipStream_t stream) {
   return launch_status();
 }
 
+template <int P, class Io, bool INV>
+int launch_rdfft_long(void* data, int64_t rows, hipStream_t stream) {
+  constexpr int E = long_elems(P);
+  const size_t lds = static_cast<size_t>(Row<P, E>::LDS) * sizeof(float);
+  if (rows > 0x7fffffff) return RDFFT_ERR_SIZE;
+  auto* d = static_cast<typename Io::T*>(data);
+  if (INV)
+    rdfft_inv_long_kernel<P, Io><<<dim3(static_cast<unsigned>(rows)), dim3(P / E), lds, stream>>>(d);
+  else
+    rdfft_fwd_long_kernel<P, Io><<<dim3(static_cast<unsigned>(rows)), dim3(P / E), lds, stream>>>(d);
+  return launch_status();
+}
+
 template <class Io, bool INV>
 int dispatch_rdfft(void* data, int64_t rows, int64_t p, hipStream_t s) {
   switch (p) {
@@ -57,6 +70,9 @@ int dispatch_rdfft(void* data, int64_t rows, int64_t p, hipStream_t s) {
     case 1024: return launch_rdfft<1024, Io, INV>(data, rows, s);
     case 2048: return launch_rdfft<2048, Io, INV>(data, rows, s);
     case 4096: return launch_rdfft<4096, Io, INV>(data, rows, s);
+    case 8192: return launch_rdfft_long<8192, Io, INV>(data, rows, s);
+    case 16384: return launch_rdfft_long<16384, Io, INV>(data, rows, s);
+    case 32768: return launch_rdfft_long<32768, Io, INV>(data, rows, s);
     default: return RDFFT_ERR_SIZE;
   }
 }
@@ -280,7 +296,9 @@ const char* rdfft_status_string(int status) {
   switch (status) {
     case RDFFT_OK: return "ok";
     case RDFFT_ERR_NULL: return "null pointer";
-    case RDFFT_ERR_SIZE: return "unsupported size (p must be a power of two in [2, 4096]; counts >= 0)";
+    case RDFFT_ERR_SIZE:
+      return "unsupported size (p a power of two in [2, 32768] for transforms and spectra, [2, 4096] for "
+             "circulant layers; counts >= 0)";
     case RDFFT_ERR_SHAPE: return "d_in and d_out must be positive multiples of p";
     case RDFFT_ERR_DTYPE: return "unknown dtype (RDFFT_F32, RDFFT_BF16 or RDFFT_F16)";
     case RDFFT_ERR_ALIGN: return "pointer not 16-byte aligned";

@@ -10,7 +10,8 @@
 
 namespace rdfft {
 
-inline bool valid_len(int64_t p) { return p >= 2 && p <= 4096 && (p & (p - 1)) == 0; }
+// row lengths: transforms and spectrum utilities up to 32768, circulant blocks up to 4096
+inline bool valid_len(int64_t p, int64_t pmax = 32768) { return p >= 2 && p <= pmax && (p & (p - 1)) == 0; }
 inline bool valid_dtype(int dtype) { return dtype == RDFFT_F32 || dtype == RDFFT_BF16 || dtype == RDFFT_F16; }
 inline int64_t dtype_bytes(int dtype) { return dtype == RDFFT_F32 ? 4 : 2; }
 inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -46,7 +47,7 @@ inline int check_spectrum(const void* packed, const float* spec, int64_t rows, i
 }
 
 inline int check_circulant_dims(int64_t batch, int64_t d_in, int64_t d_out, int64_t p) {
-  if (!valid_len(p) || batch < 0) return RDFFT_ERR_SIZE;
+  if (!valid_len(p, 4096) || batch < 0) return RDFFT_ERR_SIZE;
   if (d_in <= 0 || d_out <= 0 || d_in % p != 0 || d_out % p != 0) return RDFFT_ERR_SHAPE;
   if (d_in > kMaxElems || d_out > kMaxElems || batch > kMaxElems / d_in || batch > kMaxElems / d_out ||
       (d_in / p) > kMaxElems / d_out)

@@ -29,7 +29,9 @@
  *     half).  All arithmetic is fp32; 16-bit results are rounded to nearest
  *     even once, on store.  The circulant parameters c, their gradient dc and
  *     explicit complex spectra are always float.
- *   - Supported row / block lengths: p = 2, 4, 8, ..., 4096.
+ *   - Supported lengths: transforms and spectrum utilities p = 2, 4, 8, ...,
+ *     32768 (a row is staged in one workgroup's LDS; the pages stop at 4096);
+ *     circulant blocks p = 2, 4, ..., 4096.
  *   - Non-finite inputs are propagated, not checked.
  */
 #ifndef RDFFT_H
@@ -51,7 +53,7 @@ extern "C" {
 /* status codes */
 #define RDFFT_OK 0
 #define RDFFT_ERR_NULL 1   /* a required pointer is NULL */
-#define RDFFT_ERR_SIZE 2   /* p not a power of two in [2, 4096], or a negative / too large count */
+#define RDFFT_ERR_SIZE 2   /* p not a supported power of two, or a negative / too large count */
 #define RDFFT_ERR_SHAPE 3  /* d_in or d_out not a positive multiple of p */
 #define RDFFT_ERR_DTYPE 4  /* dtype not RDFFT_F32 / RDFFT_BF16 / RDFFT_F16 */
 #define RDFFT_ERR_ALIGN 5  /* a pointer is not 16-byte aligned */

@@ -70,10 +70,11 @@ def test_rdfft_validation(L, fn):
     assert f(None, 4, 512, F32, None) == NULL
     assert f(None, 0, 512, F32, None) == OK  # empty batch: no-op, pointer unchecked
     assert f(A, 0, 4096, BF16, None) == OK
-    for p in (0, 1, 3, 6, 100, 8192, -4):
+    for p in (0, 1, 3, 6, 100, 65536, -4):
         assert f(A, 4, p, F32, None) == SIZE, p
     assert f(A, -1, 512, F32, None) == SIZE
     assert f(A, 1 << 40, 4096, F32, None) == SIZE  # element count too large
+    assert f(A, 1 << 26, 32768, F32, None) == SIZE
     assert f(A, 4, 512, 3, None) == DTYPE
     assert f(A, 4, 512, -1, None) == DTYPE
     assert f(None, 4, 512, F16, None) == NULL
@@ -125,7 +126,7 @@ def test_spectrum_validation(L, fn):
     assert f(A, B_, 0, 512, F32, None) == OK  # empty: no-op
     assert f(None, B_, 4, 512, F32, None) == NULL
     assert f(A, None, 4, 512, BF16, None) == NULL
-    for p in (0, 1, 3, 8192):
+    for p in (0, 1, 3, 65536):
         assert f(A, B_, 4, p, F32, None) == SIZE, p
     assert f(A, B_, -2, 512, F32, None) == SIZE
     assert f(A, B_, 4, 512, 7, None) == DTYPE

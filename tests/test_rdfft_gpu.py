@@ -17,7 +17,7 @@ from tests.gpu_util import TOL, TORCH_DT, device_input, row_relerr, to_f64
 
 pytestmark = pytest.mark.gpu
 
-ALL_P = [2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
+ALL_P = [2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768]
 
 
 def _say(*a):
@@ -64,7 +64,7 @@ def test_empty_batch_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("p", [2, 16, 512, 4096])
+@pytest.mark.parametrize("p", [2, 16, 512, 4096, 32768])
 def test_closed_forms_on_gpu(p):
     n = np.arange(p)
     rows = np.stack([np.eye(1, p, 0)[0], np.ones(p), (-1.0) ** n, np.cos(2 * np.pi * n / p), np.sin(2 * np.pi * n / p)])
@@ -84,7 +84,7 @@ def test_closed_forms_on_gpu(p):
     assert np.allclose(got, want, atol=2e-6 * p)
 
 
-@pytest.mark.parametrize("p", [128, 4096])
+@pytest.mark.parametrize("p", [128, 4096, 16384])
 def test_inverse_accepts_any_packed_vector(p):
     z, zref = device_input((64, p), syn.WL_TEST, syn.T_DY, p)
     bcl.rdfft_inverse(z)
@@ -92,7 +92,7 @@ def test_inverse_accepts_any_packed_vector(p):
     assert row_relerr(to_f64(z), ro.rdfft_inverse(zref)) <= 1e-5
 
 
-@pytest.mark.parametrize("p,dtype", [(512, "f32"), (4096, "bf16")])
+@pytest.mark.parametrize("p,dtype", [(512, "f32"), (4096, "bf16"), (32768, "f32")])
 def test_bitwise_deterministic(p, dtype):
     x, _ = device_input((1024, p), syn.WL_TEST, syn.T_X, 7, dtype=dtype)
     outs = []
@@ -133,6 +133,13 @@ def test_workload_4096x4096(dtype):
 def test_workload_16384x128(dtype):
     ef, ei = _check_fwd_inv(16384, 128, dtype, syn.WL_RDFFT_LARGE, index=1)
     _say(f"16384x128 {dtype}: fwd {ef:.2e} inv {ei:.2e}")
+
+
+@pytest.mark.parametrize("rows,p", [(2048, 8192), (512, 32768)])
+def test_long_rows_64mib(rows, p):
+    # 64 MiB of fp32 rows longer than 4096: one workgroup per row
+    ef, ei = _check_fwd_inv(rows, p, "f32", syn.WL_RDFFT_LARGE, index=p)
+    _say(f"{rows}x{p} f32: fwd {ef:.2e} inv {ei:.2e}")
 
 
 def test_no_device_allocation():

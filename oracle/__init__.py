@@ -24,8 +24,12 @@ Modules
                    Python loops, for small rows.  Pins the reading of the pages.
   circulant_oracle block-circulant layer forward / backward, once as the dense
                    matrix definition and once as the pages' FFT formula.
+  rdfft2d_oracle   the 2D extension (packed along each axis where the data is
+                   conjugate-symmetric), as the 2D DFT definition plus its
+                   packing rule.
 
-Every function here is pinned by ``tests/test_oracle.py`` against something
+Every function here is pinned by ``tests/test_oracle.py`` (2D:
+``tests/test_oracle2d.py``) against something
 other than itself (brute-force DFT, closed forms, the pages' worked index
 example, finite differences, invariants).  No function is "parity unpinned".
 """

@@ -200,6 +200,37 @@ def bench_spectrum(rows, p, steps, warmup):
     return out
 
 
+def bench_rdfft2d(h, w, steps, warmup):
+    """2D forward then inverse in place over a rotating set of h x w fp32
+    arrays; GB/s on the algorithmic bytes (each array read and written once per
+    transform), although the transform makes three passes over the array."""
+    nbytes = h * w * 4
+    nbuf = max(2, ROTATE_BYTES // nbytes)
+    bufs = [syn.torch_normal((h, w), syn.WL_RDFFT_LARGE, syn.T_X, 50 + i) for i in range(nbuf)]
+    gf = _replayer(lambda: [bcl.rdfft2d_forward(b) for b in bufs], False)
+    gi = _replayer(lambda: [bcl.rdfft2d_inverse(b) for b in bufs], False)
+    for _ in range(max(1, -(-warmup // nbuf))):
+        gf()
+        gi()
+    reps = max(1, -(-steps // nbuf))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        ev[r][0].record()
+        gf()
+        ev[r][1].record()
+        gi()
+        ev[r][2].record()
+    torch.cuda.synchronize()
+    fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / (reps * nbuf)
+    inv = sum(e[1].elapsed_time(e[2]) for e in ev) / (reps * nbuf)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"fwd_ms": round(fwd, 5), "inv_ms": round(inv, 5),
+            "fwd_gbs_algorithmic": round(2 * nbytes / (fwd * 1e-3) / 1e9, 1),
+            "inv_gbs_algorithmic": round(2 * nbytes / (inv * 1e-3) / 1e9, 1)}
+
+
 def bench_copy(nbytes, steps, warmup):
     """A plain device copy of nbytes (torch copy_, one read and one write of
     every byte) over the same 1 GiB rotation: the practical ceiling a transform
@@ -458,6 +489,8 @@ def main():
                 "fwd_kernel_ms": round(e["fwd_ms"], 5),
                 "inv_kernel_ms": round(e["inv_ms"], 5),
             }
+        log("extra: 2D 4096x4096 f32")
+        extra["rdfft2d_4096x4096_f32"] = bench_rdfft2d(4096, 4096, 256, 32)
         log("extra: unpack / pack 4096x512 f32")
         extra["spectrum_unpack_pack_4096x512_f32"] = bench_spectrum(4096, 512, 1024, 128)
         for mib in (8, 64):

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     circulant_fwd,
     lib,
     lib_path,
+    rdfft2d_forward,
+    rdfft2d_inverse,
     rdfft_forward,
     rdfft_inverse,
     rdfft_pack,

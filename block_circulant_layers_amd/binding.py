@@ -28,6 +28,8 @@ __all__ = [
     "RDFFT_F16",
     "rdfft_unpack",
     "rdfft_pack",
+    "rdfft2d_forward",
+    "rdfft2d_inverse",
 ]
 
 RDFFT_F32 = 0
@@ -49,6 +51,8 @@ SIGNATURES = {
     "circulant_bwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_unpack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_pack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
+    "rdfft2d_forward": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "rdfft2d_inverse": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
 }
 
 
@@ -201,3 +205,27 @@ def rdfft_pack(spec: torch.Tensor, packed: torch.Tensor, stream=None) -> torch.T
         raise ValueError("spec must be float32 of shape (..., p/2 + 1, 2)")
     _call("rdfft_pack", spec.data_ptr(), packed.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
     return packed
+
+
+def _dims2d(data: torch.Tensor):
+    if data.dim() < 2:
+        raise ValueError("2D transforms need (..., h, w) tensors")
+    h, w = data.shape[-2], data.shape[-1]
+    n = data.numel() // (h * w) if h * w else 0
+    return n, h, w
+
+
+def rdfft2d_forward(data: torch.Tensor, stream=None) -> torch.Tensor:
+    """In-place packed 2D forward transform of the last two axes of ``data``."""
+    _check_gpu(data)
+    n, h, w = _dims2d(data)
+    _call("rdfft2d_forward", data.data_ptr(), n, h, w, _dtype_code(data), _stream(data, stream))
+    return data
+
+
+def rdfft2d_inverse(data: torch.Tensor, stream=None) -> torch.Tensor:
+    """In-place inverse of :func:`rdfft2d_forward` (carries 1/(h w))."""
+    _check_gpu(data)
+    n, h, w = _dims2d(data)
+    _call("rdfft2d_inverse", data.data_ptr(), n, h, w, _dtype_code(data), _stream(data, stream))
+    return data

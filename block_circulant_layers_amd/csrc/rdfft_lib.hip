@@ -6,6 +6,7 @@
 #include "circulant_kernels.hpp"
 #include "rdfft_validate.hpp"
 #include "spectrum_kernels.hpp"
+#include "rdfft2d_kernels.hpp"
 
 namespace rdfft {
 namespace {
@@ -267,6 +268,66 @@ unsigned elementwise_grid(int64_t total) {
   return static_cast<unsigned>(want < cap ? want : cap);
 }
 
+// ---- 2D ----------------------------------------------------------------------
+
+template <int H, class Io, bool INV>
+int launch_cols(void* data, int64_t n, int64_t w, hipStream_t s) {
+  constexpr int C = col_tile(H);
+  const int64_t ntiles = (w + C - 1) / C;
+  if (n * ntiles > 0x7fffffff) return RDFFT_ERR_SIZE;
+  const size_t lds = static_cast<size_t>(C) * col_stride<H>() * sizeof(float);
+  col_kernel<H, INV, Io><<<dim3(static_cast<unsigned>(n * ntiles)), dim3(C * (H / elems_per_thread(H))), lds, s>>>(
+      static_cast<typename Io::T*>(data), static_cast<int>(w), static_cast<int>(ntiles));
+  return launch_status();
+}
+
+template <class Io, bool INV>
+int dispatch_cols(void* data, int64_t n, int64_t h, int64_t w, hipStream_t s) {
+  switch (h) {
+    case 2: return launch_cols<2, Io, INV>(data, n, w, s);
+    case 4: return launch_cols<4, Io, INV>(data, n, w, s);
+    case 8: return launch_cols<8, Io, INV>(data, n, w, s);
+    case 16: return launch_cols<16, Io, INV>(data, n, w, s);
+    case 32: return launch_cols<32, Io, INV>(data, n, w, s);
+    case 64: return launch_cols<64, Io, INV>(data, n, w, s);
+    case 128: return launch_cols<128, Io, INV>(data, n, w, s);
+    case 256: return launch_cols<256, Io, INV>(data, n, w, s);
+    case 512: return launch_cols<512, Io, INV>(data, n, w, s);
+    case 1024: return launch_cols<1024, Io, INV>(data, n, w, s);
+    case 2048: return launch_cols<2048, Io, INV>(data, n, w, s);
+    case 4096: return launch_cols<4096, Io, INV>(data, n, w, s);
+    default: return RDFFT_ERR_SIZE;
+  }
+}
+
+template <class Io, bool INV>
+int launch_combine(void* data, int64_t n, int64_t h, int64_t w, hipStream_t s) {
+  if (h < 4 || w < 4) return RDFFT_OK;  // no pair (j, k) with 0 < j < h/2 and 0 < k < w/2
+  const int64_t total = n * (h / 2) * (w / 2);
+  combine_kernel<INV, Io><<<dim3(elementwise_grid(total)), dim3(256), 0, s>>>(
+      static_cast<typename Io::T*>(data), n, ilog2(static_cast<int>(h)), ilog2(static_cast<int>(w)));
+  return launch_status();
+}
+
+template <bool INV>
+int rdfft2d_entry(void* data, int64_t n, int64_t h, int64_t w, int dtype, void* stream) {
+  const int st = check_rdfft2d(data, n, h, w, dtype);
+  if (st != RDFFT_OK || n == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return by_dtype(dtype, [&](auto io) {
+    using Io = decltype(io);
+    int r;
+    if (!INV) {
+      if ((r = dispatch_rdfft<Io, false>(data, n * h, w, s)) != RDFFT_OK) return r;
+      if ((r = dispatch_cols<Io, false>(data, n, h, w, s)) != RDFFT_OK) return r;
+      return launch_combine<Io, false>(data, n, h, w, s);
+    }
+    if ((r = launch_combine<Io, true>(data, n, h, w, s)) != RDFFT_OK) return r;
+    if ((r = dispatch_cols<Io, true>(data, n, h, w, s)) != RDFFT_OK) return r;
+    return dispatch_rdfft<Io, true>(data, n * h, w, s);
+  });
+}
+
 template <bool PACK>
 int spectrum_entry(const void* packed, const float* spec, int64_t rows, int64_t p, int dtype, void* stream) {
   const int st = check_spectrum(packed, spec, rows, p, dtype);
@@ -342,6 +403,14 @@ int rdfft_unpack(const void* packed, float* spec, int64_t rows, int64_t p, int d
 
 int rdfft_pack(const float* spec, void* packed, int64_t rows, int64_t p, int dtype, void* stream) {
   return rdfft::spectrum_entry<true>(packed, spec, rows, p, dtype, stream);
+}
+
+int rdfft2d_forward(void* data, int64_t n, int64_t h, int64_t w, int dtype, void* stream) {
+  return rdfft::rdfft2d_entry<false>(data, n, h, w, dtype, stream);
+}
+
+int rdfft2d_inverse(void* data, int64_t n, int64_t h, int64_t w, int dtype, void* stream) {
+  return rdfft::rdfft2d_entry<true>(data, n, h, w, dtype, stream);
 }
 
 }  // extern "C"

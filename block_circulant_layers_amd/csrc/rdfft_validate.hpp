@@ -46,6 +46,16 @@ inline int check_spectrum(const void* packed, const float* spec, int64_t rows, i
   return RDFFT_OK;
 }
 
+// n arrays of h x w (h <= 4096: the column transforms stage a column in LDS)
+inline int check_rdfft2d(const void* data, int64_t n, int64_t h, int64_t w, int dtype) {
+  if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;
+  if (!valid_len(h, 4096) || !valid_len(w) || n < 0 || n > kMaxElems / (h * w)) return RDFFT_ERR_SIZE;
+  if (n == 0) return RDFFT_OK;
+  if (data == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(data)) return RDFFT_ERR_ALIGN;
+  return RDFFT_OK;
+}
+
 inline int check_circulant_dims(int64_t batch, int64_t d_in, int64_t d_out, int64_t p) {
   if (!valid_len(p, 4096) || batch < 0) return RDFFT_ERR_SIZE;
   if (d_in <= 0 || d_out <= 0 || d_in % p != 0 || d_out % p != 0) return RDFFT_ERR_SHAPE;

@@ -141,6 +141,30 @@ int rdfft_unpack(const void* packed, float* spec, int64_t rows, int64_t p, int d
  */
 int rdfft_pack(const float* spec, void* packed, int64_t rows, int64_t p, int dtype, void* stream);
 
+/*
+ * rdfft2d_forward -- in-place 2D forward transform of n real arrays of h x w
+ * (the 2D extension the pages leave open, Paper-Notes page "局限与展望").
+ *   data [n, h, w] of dtype; on return each array holds its 2D DFT
+ *        Y[j, k] = sum_{a, b} x[a, b] exp(-2 pi i (j a / h + k b / w)) for
+ *        k = 0..w/2 (the rest is conjugate), packed along each axis where the
+ *        data is conjugate-symmetric:
+ *          columns k = 0 and k = w/2: Y[., k] in the 1D packed layout along j
+ *            ([0, k] = Y[0, k], [h/2, k] = Y[h/2, k], [j, k] = Re Y[j, k],
+ *            [h-j, k] = Im Y[j, k] for 0 < j < h/2);
+ *          0 < k < w/2: [j, k] = Re Y[j, k] and [j, w-k] = Im Y[j, k], every j.
+ *   h: power of two in [2, 4096]; w: power of two in [2, 32768]; unnormalised.
+ *   Three in-place passes over data (row transforms, column transforms, a
+ *   combine of column pairs); 16-bit dtypes are rounded to storage after each.
+ */
+int rdfft2d_forward(void* data, int64_t n, int64_t h, int64_t w, int dtype, void* stream);
+
+/*
+ * rdfft2d_inverse -- in-place inverse of rdfft2d_forward (carries 1/(h w)).
+ *   data [n, h, w] of dtype in the layout above; any h*w reals are a valid
+ *   packed 2D spectrum.  The three passes run in reverse order.
+ */
+int rdfft2d_inverse(void* data, int64_t n, int64_t h, int64_t w, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

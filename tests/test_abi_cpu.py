@@ -38,7 +38,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = _header_functions()
     assert set(names) == {"rdfft_abi_version", "rdfft_status_string", "rdfft_forward", "rdfft_inverse",
-                          "circulant_fwd", "circulant_bwd", "rdfft_unpack", "rdfft_pack"}
+                          "circulant_fwd", "circulant_bwd", "rdfft_unpack", "rdfft_pack",
+                          "rdfft2d_forward", "rdfft2d_inverse"}
     for n in names:
         assert hasattr(L, n), n
     # the binding's signature table covers exactly the header
@@ -135,6 +136,19 @@ def test_spectrum_validation(L, fn):
     # 4 rows of 512 floats = 8 KiB packed; 4 x 257 x 8 B spectra
     assert f(A, ctypes.c_void_p(0x100000 + 4096), 4, 512, F32, None) == ALIAS
     assert f(ctypes.c_void_p(0x200000 + 8176), B_, 4, 512, F32, None) == ALIAS
+
+
+@pytest.mark.parametrize("fn", ["rdfft2d_forward", "rdfft2d_inverse"])
+def test_rdfft2d_validation(L, fn):
+    f = getattr(L, fn)
+    assert f(None, 0, 64, 64, F32, None) == OK  # no arrays: no-op
+    assert f(None, 2, 64, 64, F32, None) == NULL
+    for h, w in ((3, 64), (64, 3), (8192, 64), (64, 65536), (1, 64), (64, 1)):
+        assert f(A, 2, h, w, F32, None) == SIZE, (h, w)
+    assert f(A, -1, 64, 64, F32, None) == SIZE
+    assert f(A, 1 << 30, 4096, 4096, F32, None) == SIZE
+    assert f(A, 2, 64, 64, 5, None) == DTYPE
+    assert f(ctypes.c_void_p(0x100002), 2, 64, 64, F16, None) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -373,6 +373,9 @@ __host__ __device__ constexpr bool class_fast(int P, int B) { return B == 128 &&
 // Loaders are called as ld(var, cst) for element var + cst (var varies per
 // lane, cst is a compile-time constant); storers as st(var, cst, value).
 // ---------------------------------------------------------------------------
+// twiddle placements of kernels that run both directions (Row::TwSet)
+constexpr int kTwRegs = 0, kTwLds = 1, kTwRegsFwd = 2;
+
 template <int P, int E>
 struct Row {
   static_assert((P & (P - 1)) == 0 && P >= 2 && P <= 32768, "P must be a power of two in [2, 32768]");
@@ -508,10 +511,12 @@ struct Row {
   };
 
   // Both directions' twiddles for a kernel that runs forward and inverse
-  // transforms: register copies (IN_LDS false) or one LDS table of
-  // lds_floats() floats that init() fills cooperatively (a barrier must follow
-  // before the first transform).
-  template <bool IN_LDS, int D = 0>
+  // transforms, by placement: kTwRegs (register copies of both tables),
+  // kTwLds (one LDS table of lds_floats() floats that init() fills
+  // cooperatively; a barrier must follow before the first transform) or
+  // kTwRegsFwd (registers for the forward (cos, tan) only; the inverse takes
+  // sin = cos * tan from them, half the registers of kTwRegs).
+  template <int MODE, int D = 0>
   struct TwSet {
     FwdTws f;
     InvTws i;
@@ -524,7 +529,7 @@ struct Row {
     __device__ __forceinline__ const InvTws& inv() const { return i; }
   };
   template <int D>
-  struct TwSet<true, D> {
+  struct TwSet<kTwLds, D> {
     LdsTws l;
     static constexpr int lds_floats() { return (2 * LdsTws::entries() + 3) / 4 * 4; }
     __device__ __forceinline__ void init(TwF* dst, int tid, int nt, int) {
@@ -533,6 +538,24 @@ struct Row {
     }
     __device__ __forceinline__ const LdsTws& fwd() const { return l; }
     __device__ __forceinline__ const LdsTws& inv() const { return l; }
+  };
+  struct InvFromFwd {
+    const FwdTws& f;
+    template <int B, class WW, int RR>
+    __device__ __forceinline__ void item(int n, int k, WW (&out)[RR]) const {
+      TwF src[RR];
+      f.template item<B>(n, k, src);
+#pragma unroll
+      for (int j = 0; j < RR; ++j) out[j] = Tw{src[j].c, src[j].c * src[j].tn};
+    }
+  };
+  template <int D>
+  struct TwSet<kTwRegsFwd, D> {
+    FwdTws f;
+    static constexpr int lds_floats() { return 0; }
+    __device__ __forceinline__ void init(TwF*, int, int, int t) { f.load(t); }
+    __device__ __forceinline__ const FwdTws& fwd() const { return f; }
+    __device__ __forceinline__ InvFromFwd inv() const { return InvFromFwd{f}; }
   };
 
   // ---- forward ----------------------------------------------------------

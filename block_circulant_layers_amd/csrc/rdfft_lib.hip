@@ -125,8 +125,7 @@ int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int6
 }
 
 constexpr int64_t kMaxLds = 160 * 1024;
-constexpr int64_t kTargetWgs = 256;    // workgroups per launch of the token-persistent kernels
-constexpr int64_t kDctpTargetWgs = 256;  // the same for the dc kernel
+constexpr int64_t kTargetWgs = 256;  // workgroups per launch of the token-persistent kernels
 
 // token split: about `target` workgroups over `tiles` weight tiles, tpw a multiple of tb
 int64_t tokens_per_wg(int64_t batch, int64_t tiles, int tb, int64_t target = kTargetWgs) {
@@ -175,7 +174,7 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
     using S = DtpShape<P>;
     const int64_t gy = (q + S::K.ti - 1) / S::K.ti, gz = (k + S::K.tj - 1) / S::K.tj;
     if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
-    const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb, kDctpTargetWgs);
+    const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb, S::K.wgs);
     const int64_t gx = (batch + tpw - 1) / tpw;
     if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
     int st = zeroed ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);

@@ -358,11 +358,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const typename Io::T
 
 // ---------------------------------------------------------------------------
 // exchange layouts: padding of layout B and item order of the pass reading
-// layout B, for rows of P with E = 16 per thread.  Chosen by simulating the
-// 32-bank conflicts of every LDS access of the pass schedule.
+// layout B, for rows of P with E = 16 per thread (B = 32: E = 32).  Chosen by
+// simulating the 32-bank conflicts of every LDS access of the pass schedule.
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int lds_pad(int P, int B) {
-  return B <= 16 ? 1 : B == 128 ? (P <= 512 ? 8 : P == 1024 ? 4 : P == 2048 ? 2 : 1) : 0;
+  return B <= 16 || B == 32 ? 1 : B == 128 ? (P <= 512 ? 8 : P == 1024 ? 4 : P == 2048 ? 2 : 1) : 0;
 }
 // true: items of the pass with input size B are numbered class-fastest
 // (k = item % (B/2)); false: residue-fastest (r' = item % NRES)

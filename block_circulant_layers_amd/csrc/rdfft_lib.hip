@@ -29,7 +29,7 @@ int device_cus() {
 
 template <int P, class Io, bool INV>
 int launch_rdfft(void* data, int64_t rows, hipStream_t stream) {
-  constexpr int E = elems_per_thread(P);
+  constexpr int E = standalone_elems(P, is_f32_io<Io>());
   constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / (P / E);
   const int64_t groups = (rows + ROWS - 1) / ROWS;

@@ -97,6 +97,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _check_gpu(*ts: torch.Tensor) -> None:
+    dev = None
     for t in ts:
         if t is None:
             continue
@@ -104,6 +105,9 @@ def _check_gpu(*ts: torch.Tensor) -> None:
             raise ValueError("tensors must be on a GPU (there is no CPU path)")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if dev is not None and t.device != dev:
+            raise ValueError("tensors must be on one device")
+        dev = t.device
 
 
 def _stream(t: torch.Tensor, stream) -> int:
@@ -114,8 +118,10 @@ def _stream(t: torch.Tensor, stream) -> int:
     return int(stream)
 
 
-def _call(name: str, *args) -> None:
-    st = getattr(lib(), name)(*args)
+def _call(name: str, device: torch.device, *args) -> None:
+    # launches go to the current HIP device: make it the tensors' device
+    with torch.cuda.device(device):
+        st = getattr(lib(), name)(*args)
     if st != 0:
         raise RdfftError(name, st)
 
@@ -125,7 +131,7 @@ def rdfft_forward(data: torch.Tensor, stream=None) -> torch.Tensor:
     _check_gpu(data)
     p = data.shape[-1] if data.dim() else 0
     rows = data.numel() // p if p else 0
-    _call("rdfft_forward", data.data_ptr(), rows, p, _dtype_code(data), _stream(data, stream))
+    _call("rdfft_forward", data.device, data.data_ptr(), rows, p, _dtype_code(data), _stream(data, stream))
     return data
 
 
@@ -134,7 +140,7 @@ def rdfft_inverse(data: torch.Tensor, stream=None) -> torch.Tensor:
     _check_gpu(data)
     p = data.shape[-1] if data.dim() else 0
     rows = data.numel() // p if p else 0
-    _call("rdfft_inverse", data.data_ptr(), rows, p, _dtype_code(data), _stream(data, stream))
+    _call("rdfft_inverse", data.device, data.data_ptr(), rows, p, _dtype_code(data), _stream(data, stream))
     return data
 
 
@@ -156,7 +162,7 @@ def circulant_fwd(x: torch.Tensor, c: torch.Tensor, y: torch.Tensor | None = Non
     _check_gpu(x, c, y)
     if y.dtype != x.dtype:
         raise ValueError("y must have the dtype of x")
-    _call("circulant_fwd", x.data_ptr(), c.data_ptr(), y.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
+    _call("circulant_fwd", x.device, x.data_ptr(), c.data_ptr(), y.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
           _stream(x, stream))
     return y
 
@@ -174,7 +180,7 @@ def circulant_bwd(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: torch.
         raise ValueError("dy and dx must have the dtype of x")
     if dy.numel() != batch * q * p:
         raise ValueError("dy must have shape (..., d_out)")
-    _call("circulant_bwd", x.data_ptr(), c.data_ptr(), dy.data_ptr(),
+    _call("circulant_bwd", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
           dx.data_ptr() if dx is not None else None, dc.data_ptr() if dc is not None else None,
           batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
     return dx, dc
@@ -188,10 +194,10 @@ def rdfft_unpack(packed: torch.Tensor, spec: torch.Tensor | None = None, stream=
     rows = packed.numel() // p if p else 0
     if spec is None:
         spec = torch.empty(*packed.shape[:-1], p // 2 + 1, 2, dtype=torch.float32, device=packed.device)
-    _check_gpu(spec)
+    _check_gpu(packed, spec)
     if spec.dtype != torch.float32 or spec.numel() != rows * (p + 2):
         raise ValueError("spec must be float32 of shape (..., p/2 + 1, 2)")
-    _call("rdfft_unpack", packed.data_ptr(), spec.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
+    _call("rdfft_unpack", packed.device, packed.data_ptr(), spec.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
     return spec
 
 
@@ -203,7 +209,7 @@ def rdfft_pack(spec: torch.Tensor, packed: torch.Tensor, stream=None) -> torch.T
     rows = packed.numel() // p if p else 0
     if spec.dtype != torch.float32 or spec.numel() != rows * (p + 2):
         raise ValueError("spec must be float32 of shape (..., p/2 + 1, 2)")
-    _call("rdfft_pack", spec.data_ptr(), packed.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
+    _call("rdfft_pack", packed.device, spec.data_ptr(), packed.data_ptr(), rows, p, _dtype_code(packed), _stream(packed, stream))
     return packed
 
 
@@ -219,7 +225,7 @@ def rdfft2d_forward(data: torch.Tensor, stream=None) -> torch.Tensor:
     """In-place packed 2D forward transform of the last two axes of ``data``."""
     _check_gpu(data)
     n, h, w = _dims2d(data)
-    _call("rdfft2d_forward", data.data_ptr(), n, h, w, _dtype_code(data), _stream(data, stream))
+    _call("rdfft2d_forward", data.device, data.data_ptr(), n, h, w, _dtype_code(data), _stream(data, stream))
     return data
 
 
@@ -227,5 +233,5 @@ def rdfft2d_inverse(data: torch.Tensor, stream=None) -> torch.Tensor:
     """In-place inverse of :func:`rdfft2d_forward` (carries 1/(h w))."""
     _check_gpu(data)
     n, h, w = _dims2d(data)
-    _call("rdfft2d_inverse", data.data_ptr(), n, h, w, _dtype_code(data), _stream(data, stream))
+    _call("rdfft2d_inverse", data.device, data.data_ptr(), n, h, w, _dtype_code(data), _stream(data, stream))
     return data

@@ -53,6 +53,10 @@ SHAPES = [
     (5, 8, 6, 2), (3, 16, 8, 4), (7, 24, 40, 8), (19, 48, 80, 16), (9, 96, 64, 32), (9, 128, 320, 64),
     (33, 384, 256, 128), (13, 512, 768, 256), (11, 1024, 512, 512), (6, 2048, 4096, 1024),
     (5, 2048, 4096, 2048), (3, 4096, 8192, 4096), (3, 8192, 4096, 4096),
+    # input-block counts past one transform round of the token-persistent kernel
+    # (the fallback kernels run that direction): p = 64 with 128 input blocks,
+    # p = 128 with 64, p = 1024 with 8
+    (2, 8192, 256, 64), (3, 8192, 512, 128), (2, 8192, 2048, 1024),
 ]
 
 

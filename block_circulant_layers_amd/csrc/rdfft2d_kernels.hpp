@@ -17,55 +17,87 @@
 
 namespace rdfft {
 
-// columns per workgroup of the column kernels: enough adjacent columns that a
-// wavefront reads 64-byte runs of a row, within 1024 threads
-__host__ __device__ constexpr int col_tile(int H) {
-  return cmin(1024 / (H / elems_per_thread(H)), cmax(16, 256 / (H / elems_per_thread(H))));
-}
-// LDS floats per column (odd, so the same slot of adjacent columns falls in
-// different banks)
+// Column pass.  A workgroup loads a tile of CL adjacent columns x all H rows
+// into LDS (row runs of CL elements, coalesced), transforms the columns CP at
+// a time (T = H/E threads per column, CP * T <= 1024 threads), and stores the
+// tile back the same way.  CL is the widest power of two whose tile fits the
+// LDS budget (64-byte runs from H = 2048 down, 32-byte runs at H = 4096).
 template <int H>
-__host__ __device__ constexpr int col_stride() {
-  return Row<H, elems_per_thread(H)>::LDS | 1;
-}
+struct ColShape {
+  static constexpr int E = elems_per_thread(H);
+  static constexpr int T = H / E;
+  static constexpr int CS = Row<H, E>::LDS | 1;  // odd stride: a slot of adjacent columns in different banks
+  static constexpr int CL0 = (144 * 1024) / (CS * 4);
+  static constexpr int CL = CL0 >= 64 ? 64 : CL0 >= 32 ? 32 : CL0 >= 16 ? 16 : CL0 >= 8 ? 8 : 4;
+  static constexpr int CP = cmin(CL, 1024 / T);
+  static constexpr int NT = CP * T;
+  static constexpr int NP = CL / CP;
+  static constexpr int64_t lds_bytes() { return static_cast<int64_t>(CL) * CS * 4; }
+  static_assert(CL % CP == 0 && (H * CL) % NT == 0, "column tile");
+};
 
-// Packed transforms of C = col_tile(H) adjacent columns of one image of
-// [n, H, W]: workgroup b takes tile b % ntiles of image b / ntiles.  Columns
-// past W are neither read nor written.  Each column is owned by T threads
-// (t = thread / C; c = thread % C, adjacent lanes on adjacent columns).
+// Columns of workgroup b: tile b % ntiles of image b / ntiles of [n, H, W];
+// columns past W are neither read nor written.
 template <int H, bool INV, class Io>
-__global__ void __launch_bounds__(col_tile(H) * (H / elems_per_thread(H)))
-    col_kernel(typename Io::T* __restrict__ data, int w, int ntiles) {
-  constexpr int E = elems_per_thread(H);
+__global__ void __launch_bounds__(ColShape<H>::NT) col_kernel(typename Io::T* __restrict__ data, int w, int ntiles) {
+  using S = ColShape<H>;
+  constexpr int E = S::E, T = S::T, CS = S::CS, CL = S::CL, CP = S::CP, NT = S::NT;
   using Rw = Row<H, E>;
-  constexpr int T = Rw::T;
-  constexpr int C = col_tile(H);
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
-  const int c = tid % C, t = tid / C;
-  const int col = static_cast<int>(blockIdx.x % ntiles) * C + c;
+  const int c0 = static_cast<int>(blockIdx.x % ntiles) * CL;
   const int64_t img = blockIdx.x / ntiles;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + img * H * w, static_cast<int64_t>(H) * w);
-  // element (row v + cst) of this column; columns past w aim past the image
-  const int voff = col < w ? col : H * w;
-  float* L = lds + c * col_stride<H>();
+  // tile element e: row e / CL, column c0 + e % CL (adjacent lanes on adjacent columns)
+  auto goff = [=](int e) {
+    const int col = c0 + e % CL;
+    return col < w ? (e / CL) * w + col : H * w;  // past the image: loads give 0, stores are dropped
+  };
+#pragma unroll 4
+  for (int e = tid; e < H * CL; e += NT) lds[(e % CL) * CS + e / CL] = Io::widen(Io::braw(rs, goff(e), 0));
+  __syncthreads();
+  const int t = tid % T;
   if constexpr (!INV) {
     typename Rw::FwdTws tw;
     tw.load(t);
-    row_fwd_to_lds<H>([rs, voff, w](int v, int cst) { return Io::widen(Io::braw(rs, v * w + voff, cst * w)); }, L, t,
-                      tw);
-    __syncthreads();  // the column is in L[0..H) in natural packed order
+    for (int pass = 0; pass < S::NP; ++pass) {
+      float* L = lds + (pass * CP + tid / T) * CS;
+      if constexpr (H == E) {
+        row_fwd_to_lds<H>([L](int v, int cst) { return L[v + cst]; }, L, t, tw);
+      } else {
+        float raw[E], a[E];
 #pragma unroll
-    for (int s = 0; s < E; ++s) Io::bstore(rs, (t + T * s) * w + voff, 0, L[t + T * s]);
+        for (int s = 0; s < E; ++s) raw[s] = L[t + T * s];
+        __syncthreads();  // the column's values are in registers before L is reused
+        Rw::fwd_pass0_from(a, raw, [](float v) { return v; });
+        Rw::fwd_pass0_scatter(a, L, t);
+        fwd_rest<H, E, E, true>(a, L, t, [](int, int, float) {}, tw);  // natural packed order in L
+      }
+      __syncthreads();
+    }
   } else {
     typename Rw::InvTws tw;
     tw.load(t);
+    constexpr float scale = 1.0f / static_cast<float>(H);
+    for (int pass = 0; pass < S::NP; ++pass) {
+      float* L = lds + (pass * CP + tid / T) * CS;
+      if constexpr (H == E) {
+        row_inv_from_lds<H>(L, [L](int v, int cst, float x) { L[v + cst] = x; }, t, scale, tw);
+      } else {
+        float a[E], o[E];
+        inv_rest<H, E, E, true>(a, L, t, [](int, int) { return 0.0f; }, tw);
+        Rw::inv_pass0_store(a, L, t, scale, [&o](int, int cst, float x) { o[cst / T] = x; });
+        __syncthreads();  // every read of L is done
 #pragma unroll
-    for (int s = 0; s < E; ++s) L[t + T * s] = Io::widen(Io::braw(rs, (t + T * s) * w + voff, 0));
-    __syncthreads();
-    row_inv_from_lds<H>(
-        L, [rs, voff, w](int v, int cst, float x) { Io::bstore(rs, v * w + voff, cst * w, x); }, t,
-        1.0f / static_cast<float>(H), tw);
+        for (int s = 0; s < E; ++s) L[t + T * s] = o[s];
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll 4
+  for (int e = tid; e < H * CL; e += NT) {
+    constexpr int AUX = INV ? row_store_aux_strided(64) : row_store_aux(64);
+    Io::template bstore<AUX>(rs, goff(e), 0, lds[(e % CL) * CS + e / CL]);
   }
 }
 

@@ -271,11 +271,10 @@ unsigned elementwise_grid(int64_t total) {
 
 template <int H, class Io, bool INV>
 int launch_cols(void* data, int64_t n, int64_t w, hipStream_t s) {
-  constexpr int C = col_tile(H);
-  const int64_t ntiles = (w + C - 1) / C;
+  using S = ColShape<H>;
+  const int64_t ntiles = (w + S::CL - 1) / S::CL;
   if (n * ntiles > 0x7fffffff) return RDFFT_ERR_SIZE;
-  const size_t lds = static_cast<size_t>(C) * col_stride<H>() * sizeof(float);
-  col_kernel<H, INV, Io><<<dim3(static_cast<unsigned>(n * ntiles)), dim3(C * (H / elems_per_thread(H))), lds, s>>>(
+  col_kernel<H, INV, Io><<<dim3(static_cast<unsigned>(n * ntiles)), dim3(S::NT), static_cast<size_t>(S::lds_bytes()), s>>>(
       static_cast<typename Io::T*>(data), static_cast<int>(w), static_cast<int>(ntiles));
   return launch_status();
 }

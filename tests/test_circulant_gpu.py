@@ -57,6 +57,8 @@ SHAPES = [
     # (the fallback kernels run that direction): p = 64 with 128 input blocks,
     # p = 128 with 64, p = 1024 with 8
     (2, 8192, 256, 64), (3, 8192, 512, 128), (2, 8192, 2048, 1024),
+    # a single token
+    (1, 512, 512, 64), (1, 1024, 2048, 512), (1, 4096, 4096, 4096),
 ]
 
 

@@ -30,6 +30,7 @@ def _layer_with(c: torch.Tensor) -> bcl.BlockCirculantLinear:
     (5, 96, 160, 32, "bf16", True),
     (7, 1024, 512, 128, "f32", False),
     (4, 2048, 4096, 1024, "bf16", False),
+    (6, 512, 256, 64, "f16", True),
 ])
 def test_autograd_matches_oracle(batch, d_in, d_out, p, dtype, dense):
     q, k = d_out // p, d_in // p

@@ -47,18 +47,20 @@ constexpr bool is_f32_io() {
 // Forward passes with input spectra of size B and all later ones.  The last
 // pass either stores the natural packed row through st (global) or, when
 // TO_LDS, scatters it to L[0..P) (layout P is the natural order).
+// on = false (uniform per wavefront): the wave only takes part in the
+// barriers (a wave whose rows are all padding skips their arithmetic).
 template <int P, int E, int B, bool TO_LDS, class St, class TW>
-__device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, const TW& tw) {
+__device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, const TW& tw, bool on = true) {
   using Rw = Row<P, E>;
   using PS = typename Rw::template Pass<B>;
   __syncthreads();  // the previous pass's scatter is visible
-  Rw::template fwd_pass<B>(a, L, t, tw);
+  if (on) Rw::template fwd_pass<B>(a, L, t, tw);
   if constexpr (PS::BP == P && !TO_LDS) {
-    Rw::template last_store<B>(a, t, st);
+    if (on) Rw::template last_store<B>(a, t, st);
   } else {
     __syncthreads();  // every gather of this exchange is done
-    Rw::template pass_scatter<B>(a, L, t);
-    if constexpr (PS::BP != P) fwd_rest<P, E, PS::BP, TO_LDS>(a, L, t, st, tw);
+    if (on) Rw::template pass_scatter<B>(a, L, t);
+    if constexpr (PS::BP != P) fwd_rest<P, E, PS::BP, TO_LDS>(a, L, t, st, tw, on);
   }
 }
 
@@ -66,23 +68,23 @@ __device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, 
 // the natural packed row through ld (global) or, when FROM_LDS, from L[0..P).
 // On return L holds the size-B spectra in layout B, synchronised.
 template <int P, int E, int B, bool FROM_LDS, class Ld, class TW>
-__device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld, const TW& tw) {
+__device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld, const TW& tw, bool on = true) {
   using Rw = Row<P, E>;
   using PS = typename Rw::template Pass<B>;
   auto from_lds = [L](int v, int c) { return L[v + c]; };
   if constexpr (PS::BP == P) {
     if constexpr (FROM_LDS) {
-      Rw::template inv_pass<B>(a, from_lds, t, tw);
+      if (on) Rw::template inv_pass<B>(a, from_lds, t, tw);
       __syncthreads();
     } else {
-      Rw::template inv_pass<B>(a, ld, t, tw);
+      if (on) Rw::template inv_pass<B>(a, ld, t, tw);
     }
   } else {
-    inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld, tw);
-    Rw::template inv_pass<B>(a, from_lds, t, tw);
+    inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld, tw, on);
+    if (on) Rw::template inv_pass<B>(a, from_lds, t, tw);
     __syncthreads();  // every gather of this exchange is done
   }
-  Rw::template inv_scatter<B>(a, L, t);
+  if (on) Rw::template inv_scatter<B>(a, L, t);
   __syncthreads();
 }
 
@@ -106,17 +108,19 @@ __device__ __forceinline__ void inv_down(float (&a)[E], float* L, int t, const T
 // after the final write.  Every thread of the workgroup must call it.
 // tw: the row's forward twiddles (Row<P, E>::FwdTws, loaded once by the caller).
 template <int P, class Ld, class TW>
-__device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW& tw) {
+__device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW& tw, bool on = true) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   float a[E];
-  Rw::fwd_pass0(a, ld, t);
+  if (on) Rw::fwd_pass0(a, ld, t);
   if constexpr (P == E) {
+    if (on) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) L[s] = a[s];
+      for (int s = 0; s < P; ++s) L[s] = a[s];
+    }
   } else {
-    Rw::fwd_pass0_scatter(a, L, t);
-    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw);
+    if (on) Rw::fwd_pass0_scatter(a, L, t);
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw, on);
   }
 }
 
@@ -124,17 +128,19 @@ __device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW&
 // widen): used where the loads were issued ahead of time.
 template <int P, class V, class Wd, class TW>
 __device__ __forceinline__ void row_fwd_raw_to_lds(const V (&raw)[elems_per_thread(P)], Wd widen, float* L, int t,
-                                                   const TW& tw) {
+                                                   const TW& tw, bool on = true) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   float a[E];
-  Rw::fwd_pass0_from(a, raw, widen);
+  if (on) Rw::fwd_pass0_from(a, raw, widen);
   if constexpr (P == E) {
+    if (on) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) L[s] = a[s];
+      for (int s = 0; s < P; ++s) L[s] = a[s];
+    }
   } else {
-    Rw::fwd_pass0_scatter(a, L, t);
-    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw);
+    if (on) Rw::fwd_pass0_scatter(a, L, t);
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw, on);
   }
 }
 
@@ -144,20 +150,22 @@ __device__ __forceinline__ void row_fwd_raw_to_lds(const V (&raw)[elems_per_thre
 // Every thread of the workgroup must call it.
 // tw: the row's inverse twiddles (Row<P, E>::InvTws, loaded once by the caller).
 template <int P, class St, class TW>
-__device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float scale, const TW& tw) {
+__device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float scale, const TW& tw, bool on = true) {
   constexpr int E = elems_per_thread(P);
   using Rw = Row<P, E>;
   float a[E];
   if constexpr (P == E) {
+    if (on) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) a[s] = L[s];
-    small_inv<P, 1>(a);
-    constexpr int LP = ilog2(P);
+      for (int s = 0; s < P; ++s) a[s] = L[s];
+      small_inv<P, 1>(a);
+      constexpr int LP = ilog2(P);
 #pragma unroll
-    for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
+      for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
+    }
   } else {
-    inv_rest<P, E, E, true>(a, L, t, [](int, int) { return 0.0f; }, tw);
-    Rw::inv_pass0_store(a, L, t, scale, st);
+    inv_rest<P, E, E, true>(a, L, t, [](int, int) { return 0.0f; }, tw, on);
+    if (on) Rw::inv_pass0_store(a, L, t, scale, st);
   }
 }
 

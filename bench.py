@@ -255,27 +255,76 @@ def bench_copy(nbytes, steps, warmup):
             "pct_hbm_peak": round(100 * 2 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
 
 
-def bench_layer_memory(batch, d, p):
-    """Peak device memory of one BlockCirculantLinear forward + backward in
-    fp32, counted from an empty allocator: parameters c, their gradient, x,
-    y, dy and dx (the quantities a single-layer peak-memory figure holds),
-    and what the step needed beyond those tensors (workspace)."""
+def torch_fft_circulant(x, c, real):
+    """Context only, never a product path: the block-circulant layer in the
+    form its baselines take on the pages (Paper-Notes, "实验关键数据"; scime,
+    "Measured effects reported in the paper"): y_i = IFFT(sum_j FFT(c_ij) *
+    FFT(x_j)) on torch.fft (rocFFT on this GPU), the per-block products
+    broadcast before the block sum, differentiated by autograd.  ``real``
+    picks rfft/irfft, else the complex fft/ifft."""
+    b = x.shape[0]
+    q, k, p = c.shape
+    xs = x.view(b, 1, k, p)
+    if real:
+        yf = (torch.fft.rfft(xs, dim=-1) * torch.fft.rfft(c, dim=-1)).sum(dim=2)
+        y = torch.fft.irfft(yf, n=p, dim=-1)
+    else:
+        yf = (torch.fft.fft(xs, dim=-1) * torch.fft.fft(c, dim=-1)).sum(dim=2)
+        y = torch.fft.ifft(yf, dim=-1).real
+    return y.reshape(b, q * p)
+
+
+LAYER_FORMS = {
+    "rdfft_layer": lambda x, c: bcl.BlockCirculantFunction.apply(x, c),
+    "torch_rfft": lambda x, c: torch_fft_circulant(x, c, True),
+    "torch_fft": lambda x, c: torch_fft_circulant(x, c, False),
+}
+
+
+def bench_layer_memory(batch, d, p, form="rdfft_layer"):
+    """Peak device memory of one block-circulant forward + backward in fp32,
+    counted from an empty allocator: parameters c, their gradient, x, y, dy
+    and dx (the quantities a single-layer peak-memory figure holds), and what
+    the step needed beyond those tensors (workspace).  ``form`` picks this
+    library's layer or one of the torch.fft forms run as context."""
+    fn = LAYER_FORMS[form]
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     base = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    layer = bcl.BlockCirculantLinear(d, d, p, device="cuda")
+    c = syn.torch_normal((d // p, d // p, p), syn.WL_TEST, syn.T_C, 99, scale=1 / np.sqrt(d)).requires_grad_(True)
     x = syn.torch_normal((batch, d), syn.WL_TEST, syn.T_X, 99).requires_grad_(True)
     dy = syn.torch_normal((batch, d), syn.WL_TEST, syn.T_DY, 99)
-    y = layer(x)
+    y = fn(x, c)
     y.backward(dy)
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated() - base
-    held = sum(-(-t.numel() * t.element_size() // 512) * 512 for t in (layer.c, layer.c.grad, x, x.grad, y, dy))
+    held = sum(-(-t.numel() * t.element_size() // 512) * 512 for t in (c, c.grad, x, x.grad, y, dy))
     out = {"peak_mib": round(peak / 2**20, 4), "workspace_bytes": int(peak - held)}
-    del layer, x, dy, y
+    del c, x, dy, y
     torch.cuda.empty_cache()
     return out
+
+
+def bench_layer_eager(batch, d, p, form, steps=20, warmup=3):
+    """Milliseconds per forward + backward of one fp32 layer through autograd,
+    launched eagerly (no graph), for this library's layer and the torch.fft
+    forms alike."""
+    fn = LAYER_FORMS[form]
+    c = syn.torch_normal((d // p, d // p, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0).requires_grad_(True)
+    x = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, 0).requires_grad_(True)
+    dy = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, 0)
+    for _ in range(warmup):
+        fn(x, c).backward(dy)
+    tm = Timer()
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(steps):
+        fn(x, c).backward(dy)
+    ms = tm.stop() / steps
+    del c, x, dy
+    torch.cuda.empty_cache()
+    return round(ms, 4)
 
 
 def cpu_baseline_rdfft(rows, p, seconds=10.0):
@@ -505,6 +554,18 @@ def main():
                            (256, 4096, 512), (256, 4096, 1024), (256, 4096, 4096), (1, 1024, 1024)):
             mem[f"d{d}_b{b}_p{pp}"] = bench_layer_memory(b, d, pp)
         extra["layer_peak_memory_f32"] = mem
+        log("extra: torch.fft circulant forms beside the layer (context)")
+        ctx = {"peak_mib": {}, "d4096_b256_f32_fwd_bwd_ms_eager": {}}
+        for (b, d, pp) in ((1, 4096, 128), (1, 4096, 4096), (256, 4096, 128), (256, 4096, 512), (256, 4096, 4096),
+                           (1, 1024, 1024)):
+            ctx["peak_mib"][f"d{d}_b{b}_p{pp}"] = {
+                form: (mem[f"d{d}_b{b}_p{pp}"] if form == "rdfft_layer" else bench_layer_memory(b, d, pp, form))["peak_mib"]
+                for form in LAYER_FORMS
+            }
+        for pp in (128, 512, 4096):
+            ctx["d4096_b256_f32_fwd_bwd_ms_eager"][f"p{pp}"] = {form: bench_layer_eager(256, 4096, pp, form)
+                                                               for form in LAYER_FORMS}
+        extra["torch_fft_context"] = ctx
         log("extra: 128 circulant adapters 4096x4096 p=1024, 2048 tokens")
         extra["circulant_128_adapters_d4096_p1024_b2048_bf16"] = bench_circ_adapters(10, 2)
         out["extra"] = extra

@@ -306,10 +306,11 @@ def bench_layer_memory(batch, d, p, form="rdfft_layer"):
     return out
 
 
-def bench_layer_eager(batch, d, p, form, steps=20, warmup=3):
+def bench_layer_eager(batch, d, p, form, steps=20, warmup=3, repeats=5):
     """Milliseconds per forward + backward of one fp32 layer through autograd,
     launched eagerly (no graph), for this library's layer and the torch.fft
-    forms alike."""
+    forms alike; the best of ``repeats`` timed runs of ``steps`` steps (host
+    launch overhead makes single runs noisy)."""
     fn = LAYER_FORMS[form]
     c = syn.torch_normal((d // p, d // p, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0).requires_grad_(True)
     x = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, 0).requires_grad_(True)
@@ -317,11 +318,13 @@ def bench_layer_eager(batch, d, p, form, steps=20, warmup=3):
     for _ in range(warmup):
         fn(x, c).backward(dy)
     tm = Timer()
-    torch.cuda.synchronize()
-    tm.start()
-    for _ in range(steps):
-        fn(x, c).backward(dy)
-    ms = tm.stop() / steps
+    ms = float("inf")
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(steps):
+            fn(x, c).backward(dy)
+        ms = min(ms, tm.stop() / steps)
     del c, x, dy
     torch.cuda.empty_cache()
     return round(ms, 4)

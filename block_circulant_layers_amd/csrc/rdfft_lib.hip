@@ -190,6 +190,46 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
   }
 }
 
+// dx and dc in one launch (circ_bwd_kernel) where the row length allows it and
+// the dx tiles fit; returns false when the caller must take the two-kernel path.
+constexpr int64_t kBwdDxWgs = 256;  // dx workgroups the fused token split aims at
+
+template <int P, class Io>
+bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
+                           int64_t k, int64_t q, hipStream_t s, int* status) {
+  if constexpr (bwd_fusable<P>()) {
+    using S = TpShape<P>;
+    using D = DtpShape<P>;
+    if (q > S::CR || !S::fits(static_cast<int>(q)) || S::lds_bytes(static_cast<int>(q)) > kMaxLds ||
+        k > 0x7fffffff)
+      return false;
+    const int64_t gdy = (q + D::K.ti - 1) / D::K.ti, gdz = (k + D::K.tj - 1) / D::K.tj;
+    const int64_t tpw_dc = tokens_per_wg(batch, gdy * gdz, D::K.tb, D::K.fwgs);
+    const int64_t gdx = (batch + tpw_dc - 1) / tpw_dc;
+    const int64_t gxy = (k + S::K.to - 1) / S::K.to;
+    const int64_t tpw_dx = tokens_per_wg(batch, gxy, S::K.tb, kBwdDxWgs);
+    const int64_t gxx = (batch + tpw_dx - 1) / tpw_dx;
+    const int64_t ndc = gdx * gdy * gdz, nwg = ndc + gxx * gxy;
+    if (nwg > 0x7fffffff || gdx > 0x7fffffff || gdy > 0x7fffffff || gxx > 0x7fffffff) return false;
+    const int64_t lds_dx = S::lds_bytes(static_cast<int>(q)), lds_dc = D::lds_bytes();
+    const int64_t lds = lds_dx > lds_dc ? lds_dx : lds_dc;
+    int st = launch_fill_zero(dc, q * k * P, s);
+    if (st == RDFFT_OK) {
+      circ_bwd_kernel<P, Io><<<dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt), static_cast<size_t>(lds), s>>>(
+          static_cast<const typename Io::T*>(x), c, static_cast<const typename Io::T*>(dy),
+          static_cast<typename Io::T*>(dx), dc, batch, int(k), int(q), tpw_dc, int(gdx), int(gdy), ndc, tpw_dx,
+          int(gxx));
+      st = launch_status();
+    }
+    if (st == RDFFT_OK) st = launch_rdfft<P, F32Io, true>(dc, q * k, s);
+    *status = st;
+    return true;
+  } else {
+    (void)x, (void)c, (void)dy, (void)dx, (void)dc, (void)batch, (void)k, (void)q, (void)s, (void)status;
+    return false;
+  }
+}
+
 template <int P, class Io>
 int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, hipStream_t s) {
   return launch_circ_product<P, Io>(x, c, y, batch, d_in / P, d_out / P, false, s);
@@ -200,6 +240,8 @@ int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* d
                int64_t d_out, hipStream_t s) {
   const int64_t k = d_in / P, q = d_out / P;
   if (batch == 0) return dc ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
+  int fused_status = RDFFT_OK;
+  if (dx && dc && launch_circ_bwd_fused<P, Io>(x, c, dy, dx, dc, batch, k, q, s, &fused_status)) return fused_status;
   bool zeroed = false;  // dc cleared by the dx kernel
   if (dx) {
     const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s, dc, dc ? q * k * P : 0, &zeroed);

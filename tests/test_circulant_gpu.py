@@ -110,6 +110,29 @@ def test_dc_overwritten_and_optional_outputs():
     assert row_relerr(to_f64(dx2), dxo) <= 1e-5
 
 
+@pytest.mark.parametrize("batch,d,p,dtype", [(256, 4096, 128, "bf16"), (96, 2048, 512, "f32"), (512, 4096, 1024, "bf16"),
+                                            (40, 4096, 2048, "f16"), (64, 4096, 4096, "f32")])
+def test_backward_single_outputs(batch, d, p, dtype):
+    # dx alone and dc alone take other launches than the two together (one
+    # launch holds both where the row length allows): each against the oracle
+    q = k = d // p
+    x, xr = device_input((batch, d), syn.WL_TEST, syn.T_X, p + 3, dtype=dtype)
+    c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, p + 3, scale=1 / np.sqrt(d), dtype="f32")
+    dy, dyr = device_input((batch, d), syn.WL_TEST, syn.T_DY, p + 3, dtype=dtype)
+    _say(f"circulant bwd single outputs B={batch} D={d} p={p} dtype={dtype}")
+    dxo, dco = co.circulant_backward_fft(xr, cr, dyr)
+    dx_both, dc_both = bcl.circulant_bwd(x, c, dy)
+    _, dc_only = bcl.circulant_bwd(x, c, dy, need_dx=False)
+    dx_only, _ = bcl.circulant_bwd(x, c, dy, need_dc=False)
+    torch.cuda.synchronize()
+    for dx in (dx_both, dx_only):
+        assert row_relerr(to_f64(dx), dxo) <= TOL[dtype]
+    for dc in (dc_both, dc_only):
+        assert row_relerr(to_f64(dc).reshape(-1, p), dco.reshape(-1, p)) <= TOL["f32"]
+    # the dx products are the same arithmetic in either launch
+    assert torch.equal(dx_both, dx_only)
+
+
 def test_empty_batch():
     c = torch.randn(2, 2, 16, device="cuda:0")
     x = torch.empty(0, 32, device="cuda:0")

@@ -36,8 +36,20 @@ struct ColShape {
   static_assert(CL % CP == 0 && (H * CL) % NT == 0, "column tile");
 };
 
-// Columns of workgroup b: tile b % ntiles of image b / ntiles of [n, H, W];
-// columns past W are neither read nor written.
+// Workgroups are handed to the eight XCDs in turn (workgroup b to XCD b % 8),
+// each with its own L2.  Tiles of adjacent columns share cache lines (a tile
+// row is 32 or 64 bytes at H >= 2048), so tile ids are reordered to give each
+// XCD a contiguous range: workgroups that run side by side on one XCD then
+// share lines in its L2 instead of fetching them once per XCD.  A bijection
+// of [0, total) for any total.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t total) {
+  constexpr int64_t X = 8;
+  const int64_t q = total / X, r = total % X, x = b % X, s = b / X;
+  return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+
+// Columns of workgroup b: with tile = xcd_tile(b), tile % ntiles of image
+// tile / ntiles of [n, H, W]; columns past W are neither read nor written.
 template <int H, bool INV, class Io>
 __global__ void __launch_bounds__(ColShape<H>::NT) col_kernel(typename Io::T* __restrict__ data, int w, int ntiles) {
   using S = ColShape<H>;
@@ -45,8 +57,9 @@ __global__ void __launch_bounds__(ColShape<H>::NT) col_kernel(typename Io::T* __
   using Rw = Row<H, E>;
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
-  const int c0 = static_cast<int>(blockIdx.x % ntiles) * CL;
-  const int64_t img = blockIdx.x / ntiles;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int c0 = static_cast<int>(tile % ntiles) * CL;
+  const int64_t img = tile / ntiles;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + img * H * w, static_cast<int64_t>(H) * w);
   // tile element e: row e / CL, column c0 + e % CL (adjacent lanes on adjacent columns)
   auto goff = [=](int e) {
@@ -94,11 +107,10 @@ __global__ void __launch_bounds__(ColShape<H>::NT) col_kernel(typename Io::T* __
       __syncthreads();
     }
   }
+  // default cache policy: the L2 merges the tile rows of neighbouring
+  // workgroups into whole lines before they are written back
 #pragma unroll 4
-  for (int e = tid; e < H * CL; e += NT) {
-    constexpr int AUX = INV ? row_store_aux_strided(64) : row_store_aux(64);
-    Io::template bstore<AUX>(rs, goff(e), 0, lds[(e % CL) * CS + e / CL]);
-  }
+  for (int e = tid; e < H * CL; e += NT) Io::template bstore<0>(rs, goff(e), 0, lds[(e % CL) * CS + e / CL]);
 }
 
 // The combine of column k with column W-k, 0 < k < W/2, at rows j and H-j,

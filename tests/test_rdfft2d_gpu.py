@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 TOL2D = {"f32": 1e-5, "bf16": 2e-2, "f16": 3e-3}
 SHAPES = [(3, 2, 8), (2, 8, 2), (2, 4, 4), (2, 16, 32), (2, 64, 512), (1, 1024, 1024), (1, 4096, 64),
-          (2, 128, 8192), (1, 32, 32768)]
+          (2, 128, 8192), (1, 32, 32768), (2, 4096, 16), (3, 2048, 32)]
 
 
 def _flat(a):
@@ -41,6 +41,19 @@ def test_parity(n, h, w, dtype):
     ei = row_relerr(_flat(to_f64(x)), _flat(r2.rdfft2d_inverse(z)))
     print(f"  errors fwd {ef:.2e} inv {ei:.2e}", flush=True)
     assert ef <= TOL2D[dtype] and ei <= TOL2D[dtype], (ef, ei)
+
+
+def test_full_size_4096x4096():
+    # the benchmarked array, in the launch configuration the benchmark times
+    print("rdfft2d n=1 h=4096 w=4096 f32", flush=True)
+    x, xr = device_input((1, 4096, 4096), syn.WL_TEST, syn.T_X, 4242)
+    bcl.rdfft2d_forward(x)
+    torch.cuda.synchronize()
+    z = to_f64(x)
+    assert row_relerr(_flat(z), _flat(r2.rdfft2d_forward(xr))) <= TOL2D["f32"]
+    bcl.rdfft2d_inverse(x)
+    torch.cuda.synchronize()
+    assert row_relerr(_flat(to_f64(x)), _flat(r2.rdfft2d_inverse(z))) <= TOL2D["f32"]
 
 
 @pytest.mark.parametrize("h,w", [(16, 16), (256, 128)])

@@ -439,6 +439,23 @@ def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=102
     }
 
 
+def profile_circulant(reps=3):
+    """Eager launches of the four circulant workloads (forward, then backward
+    with dx and dc), for counter collection under a profiler: no graphs, no
+    timing."""
+    for name, (batch, d, p) in {"adapter": (2048, 4096, 1024), "p128": (256, 4096, 128), "p512": (256, 4096, 512),
+                                "p4096": (256, 4096, 4096)}.items():
+        q = k = d // p
+        x = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, 0, dtype=torch.bfloat16)
+        dy = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, 0, dtype=torch.bfloat16)
+        c = syn.torch_normal((q, k, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0)
+        for _ in range(reps):
+            bcl.circulant_fwd(x, c)
+            bcl.circulant_bwd(x, c, dy)
+        torch.cuda.synchronize()
+        log(f"profiled circulant {name}: B={batch} D={d} p={p}, {reps} x (forward, backward)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,6 +471,8 @@ def main():
                     help="launch the timed transforms directly instead of from HIP graphs (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
+    ap.add_argument("--profile-circulant", action="store_true",
+                    help="only launch the circulant workloads eagerly, for counter collection, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -467,6 +486,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     bcl.lib()
+    if args.profile_circulant:
+        profile_circulant()
+        return
     if args.calib_copy:
         a = torch.ones(64 << 20, device="cuda:0")
         b = torch.empty_like(a)

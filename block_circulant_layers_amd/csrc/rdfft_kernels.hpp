@@ -44,6 +44,152 @@ constexpr bool is_f32_io() {
   return sizeof(typename Io::T) == 4;
 }
 
+// Standalone kernels whose rows are short: a wavefront access of one row
+// covers T = P/16 consecutive elements, 16 to 64 bytes for 32 <= p <= 256.
+// The rows of a workgroup's group are contiguous, so they move between HBM
+// and LDS in 16-byte pieces instead (every wavefront access covers 1 KB), and
+// the transform reads and writes its rows in LDS.  Measured (forward,
+// element-wise path -> pieces): 16384x128 fp32 6.26 -> 4.23 us, bf16 5.05 ->
+// 3.82 us; 8192x256 fp32 5.10 -> 4.55 us; 32768x64 fp32 6.95 -> 4.12 us;
+// 65536x32 bf16 10.4 -> 3.5 us.  At p = 512 (64-byte bf16 accesses, 128-byte
+// fp32) the pieces were slower for bf16 (3.98 -> 4.19 us).
+__host__ __device__ constexpr bool block_io(int P, int /*elem*/) { return P >= 32 && P <= 256; }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// The NT * E elements of a group (ROWS rows of P) as NT * CH pieces of 16
+// bytes: piece j of thread tid is bytes [16 (j NT + tid), +16) of the group,
+// elements e0 = (j NT + tid) VE .. e0 + VE - 1, all in row e0 / P.
+template <int P, class Io, int NT>
+struct BlockIo {
+  static constexpr int ELEM = static_cast<int>(sizeof(typename Io::T));
+  static constexpr int VE = 16 / ELEM;
+  static constexpr int GROUP = NT * elems_per_thread(P);
+  static constexpr int CH = GROUP / (VE * NT);
+  static_assert(GROUP % (VE * NT) == 0 && P % VE == 0, "pieces");
+  template <int AUX>
+  static __device__ __forceinline__ void load(u32x4 (&v)[CH], __amdgpu_buffer_rsrc_t rs, int tid) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * NT + tid) * 16, 0, AUX);
+  }
+  // widen into LDS rows of stride LS floats
+  static __device__ __forceinline__ void to_lds(const u32x4 (&v)[CH], float* lds, int LS, int tid) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int e0 = (j * NT + tid) * VE;
+      float* d = lds + (e0 / P) * LS + e0 % P;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (ELEM == 4) {
+          d[w] = __uint_as_float(v[j][w]);
+        } else {
+          d[2 * w] = Io::widen(static_cast<uint16_t>(v[j][w] & 0xffffu));
+          d[2 * w + 1] = Io::widen(static_cast<uint16_t>(v[j][w] >> 16));
+        }
+      }
+    }
+  }
+  // narrow from LDS rows of stride LS and store
+  template <int AUX>
+  static __device__ __forceinline__ void from_lds(const float* lds, int LS, __amdgpu_buffer_rsrc_t rs, int tid) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int e0 = (j * NT + tid) * VE;
+      const float* d = lds + (e0 / P) * LS + e0 % P;
+      u32x4 v;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (ELEM == 4)
+          v[w] = __float_as_uint(d[w]);
+        else
+          v[w] = static_cast<uint32_t>(Io::narrow(d[2 * w])) | (static_cast<uint32_t>(Io::narrow(d[2 * w + 1])) << 16);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (j * NT + tid) * 16, 0, AUX);
+    }
+  }
+};
+constexpr int kBlockLoadAux = 2, kBlockStoreAux = 2;  // streaming: every byte is touched once per launch
+
+// forward / inverse loop of the standalone kernels with block I/O (see above)
+template <int P, class Io, int NT>
+__device__ __forceinline__ void fwd_block_loop(typename Io::T* __restrict__ data, int64_t rows, float* lds) {
+  constexpr int E = elems_per_thread(P);
+  using Rw = Row<P, E>;
+  using BI = BlockIo<P, Io, NT>;
+  constexpr int T = Rw::T, ROWS = NT / T;
+  const int tid = threadIdx.x, t = tid % T;
+  float* L = lds + (tid / T) * Rw::LDS;
+  const int64_t ngroups = (rows + ROWS - 1) / ROWS, G = gridDim.x;
+  int64_t g = blockIdx.x;
+  if (g >= ngroups) return;
+  auto rsrc = [data, rows](int64_t gg) {
+    const int64_t r0 = gg * ROWS;
+    return make_rsrc<Io>(data + r0 * P, ((rows - r0 < ROWS) ? rows - r0 : ROWS) * P);
+  };
+  u32x4 v[BI::CH];
+  BI::template load<kBlockLoadAux>(v, rsrc(g), tid);
+  typename Rw::FwdTws tw;
+  tw.load(t);
+  while (true) {
+    BI::to_lds(v, lds, Rw::LDS, tid);
+    __syncthreads();
+    float a[E];
+    Rw::fwd_pass0(a, [L](int var, int c) { return L[var + c]; }, t);
+    if (g + G < ngroups) BI::template load<kBlockLoadAux>(v, rsrc(g + G), tid);
+    __syncthreads();  // every pass-0 read is done before the scatter
+    Rw::fwd_pass0_scatter(a, L, t);
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw);  // natural packed rows in LDS
+    __syncthreads();
+    BI::template from_lds<kBlockStoreAux>(lds, Rw::LDS, rsrc(g), tid);
+    g += G;
+    if (g >= ngroups) return;
+    __syncthreads();  // the stores' LDS reads are done before the next group lands
+  }
+}
+
+template <int P, class Io, int NT>
+__device__ __forceinline__ void inv_block_loop(typename Io::T* __restrict__ data, int64_t rows, float* lds) {
+  constexpr int E = elems_per_thread(P);
+  using Rw = Row<P, E>;
+  using BI = BlockIo<P, Io, NT>;
+  constexpr int T = Rw::T, ROWS = NT / T, BL = Rw::pass_in_for(P);
+  constexpr float scale = 1.0f / static_cast<float>(P);
+  const int tid = threadIdx.x, t = tid % T;
+  float* L = lds + (tid / T) * Rw::LDS;
+  const int64_t ngroups = (rows + ROWS - 1) / ROWS, G = gridDim.x;
+  int64_t g = blockIdx.x;
+  if (g >= ngroups) return;
+  auto rsrc = [data, rows](int64_t gg) {
+    const int64_t r0 = gg * ROWS;
+    return make_rsrc<Io>(data + r0 * P, ((rows - r0 < ROWS) ? rows - r0 : ROWS) * P);
+  };
+  u32x4 v[BI::CH];
+  BI::template load<kBlockLoadAux>(v, rsrc(g), tid);
+  typename Rw::InvTws tw;
+  tw.load(t);
+  while (true) {
+    BI::to_lds(v, lds, Rw::LDS, tid);
+    __syncthreads();
+    float a[E], x[E];
+    Rw::template inv_load_first<BL>(x, [L](int var, int c) { return L[var + c]; }, t);
+    Rw::template inv_first_from<BL>(a, x, [](float y) { return y; }, t, tw);
+    if (g + G < ngroups) BI::template load<kBlockLoadAux>(v, rsrc(g + G), tid);
+    __syncthreads();  // every first-pass read is done before the scatter
+    Rw::template inv_scatter<BL>(a, L, t);
+    __syncthreads();
+    inv_down<P, E, BL>(a, L, t, tw);
+    Rw::inv_pass0_store(a, L, t, scale, [&x](int, int cst, float y) { x[cst / T] = y; });
+    __syncthreads();  // every read of L is done
+#pragma unroll
+    for (int s2 = 0; s2 < E; ++s2) L[t + T * s2] = x[s2];
+    __syncthreads();
+    BI::template from_lds<kBlockStoreAux>(lds, Rw::LDS, rsrc(g), tid);
+    g += G;
+    if (g >= ngroups) return;
+    __syncthreads();  // the stores' LDS reads are done before the next group lands
+  }
+}
+
 // Forward passes with input spectra of size B and all later ones.  The last
 // pass either stores the natural packed row through st (global) or, when
 // TO_LDS, scatters it to L[0..P) (layout P is the natural order).
@@ -188,6 +334,10 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
   constexpr int ROWS = NT / T;
   constexpr int SEG = cmin(T, 64) * static_cast<int>(sizeof(typename Io::T));  // bytes per row per wave access
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
+  if constexpr (block_io(P, sizeof(typename Io::T))) {
+    fwd_block_loop<P, Io, NT>(data, rows, lds);
+    return;
+  }
   const int tid = threadIdx.x;
   const int rl = tid / T, t = tid % T;
   const int ro = rl * P;
@@ -247,6 +397,10 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
   constexpr int SEG = cmin(T, 64) * static_cast<int>(sizeof(typename Io::T));  // bytes per row per wave access
   constexpr float scale = 1.0f / static_cast<float>(P);
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
+  if constexpr (block_io(P, sizeof(typename Io::T))) {
+    inv_block_loop<P, Io, NT>(data, rows, lds);
+    return;
+  }
   const int tid = threadIdx.x;
   const int rl = tid / T, t = tid % T;
   const int ro = rl * P;

@@ -374,7 +374,7 @@ int spectrum_entry(const void* packed, const float* spec, int64_t rows, int64_t 
   if (st != RDFFT_OK || rows == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int lp = ilog2(static_cast<int>(p));
-  const unsigned grid = elementwise_grid(rows * p);
+  const unsigned grid = elementwise_grid(rows * (p / 2));  // one thread per bin below p/2
   return by_dtype(dtype, [&](auto io) {
     using Io = decltype(io);
     auto* z = static_cast<typename Io::T*>(const_cast<void*>(packed));

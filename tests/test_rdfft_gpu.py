@@ -84,6 +84,16 @@ def test_closed_forms_on_gpu(p):
     assert np.allclose(got, want, atol=2e-6 * p)
 
 
+@pytest.mark.parametrize("rows,p,dtype", [(65539, 128, "f32"), (65539, 128, "bf16"), (131075, 32, "f16"),
+                                          (40001, 256, "bf16"), (20003, 512, "f32"), (9001, 1024, "f32"),
+                                          (4099, 4096, "bf16")])
+def test_persistent_row_groups(rows, p, dtype):
+    # more row groups than resident workgroups (256 CUs x 8 one-wave workgroups
+    # of 64 / T rows for p <= 512): every workgroup loops over several groups,
+    # prefetching the next, and the last group is ragged
+    _check_fwd_inv(rows, p, dtype, index=rows)
+
+
 @pytest.mark.parametrize("p", [128, 4096, 16384])
 def test_inverse_accepts_any_packed_vector(p):
     z, zref = device_input((64, p), syn.WL_TEST, syn.T_DY, p)

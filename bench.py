@@ -594,6 +594,20 @@ def main():
         log("extra: 128 circulant adapters 4096x4096 p=1024, 2048 tokens")
         extra["circulant_128_adapters_d4096_p1024_b2048_bf16"] = bench_circ_adapters(10, 2)
         out["extra"] = extra
+        # The pages' own operator timings (Paper-Notes page, "实验关键数据";
+        # hardware, batch and precision unstated there), beside this run's
+        # launches of the same lengths: context, not a comparison of equals.
+        p4k = extra.get("rdfft_4096x4096_f32", {})
+        out["pages_context"] = {
+            "note": "pages: unnamed GPU, batch and dtype unstated; here: one MI355X, fp32, full batches",
+            "rdfft_forward_p512_ms": {"pages": 0.0279, "here_4096_rows": round(h["fwd_ms"], 5)},
+            "rdfft_inverse_p512_ms": {"pages": 0.0233, "here_4096_rows": round(h["inv_ms"], 5)},
+            "rdfft_forward_p4096_ms": {"pages": 0.0687, "here_4096_rows": p4k.get("fwd_kernel_ms")},
+            "circulant_tokens_per_s": {
+                "pages_whole_7b_finetuning": 920,
+                "here_128_adapters_only": extra["circulant_128_adapters_d4096_p1024_b2048_bf16"]["tokens_per_s"],
+            },
+        } if (rows, p, dt) == (4096, 512, "f32") else None
     print(json.dumps(out), flush=True)
 
 

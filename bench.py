@@ -552,7 +552,8 @@ def main():
                 "fwd_kernel_ms": round(e["fwd_ms"], 5),
                 "inv_kernel_ms": round(e["inv_ms"], 5),
             }
-        for (r, pp, dt) in ((4096, 4096, "f16"), (2048, 8192, "f32"), (512, 32768, "f32")):
+        for (r, pp, dt) in ((4096, 1024, "f32"), (4096, 2048, "f32"), (16384, 1024, "f32"), (4096, 4096, "f16"),
+                            (2048, 8192, "f32"), (512, 32768, "f32")):
             log(f"extra: rdfft {r}x{pp} {dt}")
             e = bench_rdfft(r, pp, dt, max(256, args.steps // 4), max(32, args.warmup // 4), syn.WL_RDFFT_LARGE)
             ach = e["bytes_per_launch"] / (e["fwd_ms"] * 1e-3) / 1e9

@@ -39,8 +39,10 @@ def test_transform_graph_replays():
         assert torch.equal(buf, eager), i
 
 
-def test_circulant_graph_replays():
-    b, d, p = 64, 1024, 128
+# p = 128: dx and dc in one launch; p = 4096: separate dx and dc kernels; p = 16:
+# the small-p kernels
+@pytest.mark.parametrize("b,d,p", [(64, 1024, 128), (32, 4096, 4096), (24, 256, 16)])
+def test_circulant_graph_replays(b, d, p):
     x, _ = device_input((b, d), syn.WL_TEST, syn.T_X, 32, dtype="bf16")
     c, _ = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 32, scale=1 / 32)
     dy, _ = device_input((b, d), syn.WL_TEST, syn.T_DY, 32, dtype="bf16")
@@ -62,3 +64,29 @@ def test_circulant_graph_replays():
         assert torch.equal(y, y0) and torch.equal(dx, dx0), i
         err = float((dc - dc0).norm() / dc0.norm())
         assert err <= 1e-5, (i, err)
+
+
+def test_2d_and_spectrum_graph_replays():
+    x0, _ = device_input((2, 256, 512), syn.WL_TEST, syn.T_X, 33)
+    eager = x0.clone()
+    bcl.rdfft2d_forward(eager)
+    spec0 = bcl.rdfft_unpack(eager)
+    back0 = torch.empty_like(eager)
+    bcl.rdfft_pack(spec0, back0)
+    buf, spec, back = x0.clone(), torch.empty_like(spec0), torch.empty_like(back0)
+
+    def step():
+        bcl.rdfft2d_forward(buf)
+        bcl.rdfft_unpack(buf, spec)
+        bcl.rdfft_pack(spec, back)
+
+    g = _capture(step)
+    for i in range(4):
+        buf.copy_(x0)  # eager work between replays
+        spec.fill_(float("nan"))
+        back.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf, eager) and torch.equal(spec, spec0) and torch.equal(back, back0), i
+    assert torch.equal(back0, eager)  # pack undoes unpack exactly

@@ -74,6 +74,28 @@ def test_grad_accumulates_and_partial_needs():
     assert torch.equal(x.grad, dx_ref)
 
 
+def test_token_axes_and_transposed_input():
+    # activations shaped (sequences, tokens, features), the leading axes being
+    # tokens alike, and a non-contiguous input (the layer makes it contiguous)
+    p, d_in, d_out = 128, 512, 256
+    q, k = d_out // p, d_in // p
+    x, xr = device_input((3, 5, d_in), syn.WL_TEST, syn.T_X, 13, dtype="bf16")
+    c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, 13, scale=1 / d_in**0.5)
+    dy, dyr = device_input((3, 5, d_out), syn.WL_TEST, syn.T_DY, 13, dtype="bf16")
+    layer = _layer_with(c)
+    xt = x.transpose(0, 1).detach().requires_grad_(True)  # (5, 3, d_in), not contiguous
+    y = layer(xt)
+    y.backward(dy.transpose(0, 1))
+    torch.cuda.synchronize()
+    assert y.shape == (5, 3, d_out)
+    xo = xr.transpose(1, 0, 2).reshape(-1, d_in)
+    dyo = dyr.transpose(1, 0, 2).reshape(-1, d_out)
+    dxo, dco = co.circulant_backward_dense(xo, cr, dyo)
+    assert row_relerr(to_f64(y).reshape(-1, d_out), co.circulant_forward_dense(xo, cr)) <= TOL["bf16"]
+    assert row_relerr(to_f64(xt.grad).reshape(-1, d_in), dxo) <= TOL["bf16"]
+    assert row_relerr(to_f64(layer.c.grad).reshape(q * k, p), dco.reshape(q * k, p)) <= TOL["f32"]
+
+
 def _nbytes(t: torch.Tensor) -> int:
     # the caching allocator rounds every block up to 512 bytes
     return -(-t.numel() * t.element_size() // 512) * 512

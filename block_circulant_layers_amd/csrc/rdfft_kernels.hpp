@@ -27,9 +27,12 @@ __host__ __device__ constexpr int wg_threads(int P, int E) {
 __host__ __device__ constexpr int standalone_elems(int P, bool /*f32*/) { return elems_per_thread(P); }
 // resident workgroups per CU the standalone kernels are launched for (fp32
 // rows of p >= 1024: two workgroups, each looping over more groups, measured
-// faster than four; a second group of look-ahead measured slower; p <= 512:
-// eight one-wave workgroups)
-__host__ __device__ constexpr int wg_per_cu(int P, bool f32) { return P >= 1024 ? (f32 ? 2 : 4) : 8; }
+// faster than four; a second group of look-ahead measured slower; 16-bit rows
+// of 1024 <= p <= 4096: four; p = 8192 (512 threads): two, as four would cap
+// registers at 64 and spill; p <= 512: eight one-wave workgroups)
+__host__ __device__ constexpr int wg_per_cu(int P, bool f32) {
+  return P >= 1024 ? (f32 || P >= 8192 ? 2 : 4) : 8;
+}
 // Forward kernels that stage the transformed row in LDS and store it in the
 // aligned element order t + T*s, instead of storing the last pass's packed
 // runs directly (their mirrored runs start one element past a line boundary,
@@ -460,7 +463,9 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
 }
 
 // ---------------------------------------------------------------------------
-// rows longer than 4096 (up to 32768, fp32 32768 = 128 KB, in one CU's LDS):
+// rows longer than 8192 (16384 and 32768; fp32 32768 = 128 KB, in one CU's
+// LDS; rows of 8192 run in the standalone kernels above, measured 2048x8192
+// fp32 30.9 -> 27.5 us forward against these):
 // one workgroup per row of P/E threads (E = 16, and 32 at 32768 to stay
 // within 1024 threads), the row in dynamic LDS between passes, each pass's
 // twiddles read from the per-pass tables as it runs.  The row is read and

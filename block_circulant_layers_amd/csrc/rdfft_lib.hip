@@ -71,7 +71,7 @@ int dispatch_rdfft(void* data, int64_t rows, int64_t p, hipStream_t s) {
     case 1024: return launch_rdfft<1024, Io, INV>(data, rows, s);
     case 2048: return launch_rdfft<2048, Io, INV>(data, rows, s);
     case 4096: return launch_rdfft<4096, Io, INV>(data, rows, s);
-    case 8192: return launch_rdfft_long<8192, Io, INV>(data, rows, s);
+    case 8192: return launch_rdfft<8192, Io, INV>(data, rows, s);  // the row (33 KB) fits static LDS
     case 16384: return launch_rdfft_long<16384, Io, INV>(data, rows, s);
     case 32768: return launch_rdfft_long<32768, Io, INV>(data, rows, s);
     default: return RDFFT_ERR_SIZE;

@@ -47,6 +47,131 @@ constexpr bool is_f32_io() {
   return sizeof(typename Io::T) == 4;
 }
 
+// Forward passes with input spectra of size B and all later ones.  The last
+// pass either stores the natural packed row through st (global) or, when
+// TO_LDS, scatters it to L[0..P) (layout P is the natural order).
+// on = false (uniform per wavefront): the wave only takes part in the
+// barriers (a wave whose rows are all padding skips their arithmetic).
+template <int P, int E, int B, bool TO_LDS, class St, class TW>
+__device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, const TW& tw, bool on = true) {
+  using Rw = Row<P, E>;
+  using PS = typename Rw::template Pass<B>;
+  __syncthreads();  // the previous pass's scatter is visible
+  if (on) Rw::template fwd_pass<B>(a, L, t, tw);
+  if constexpr (PS::BP == P && !TO_LDS) {
+    if (on) Rw::template last_store<B>(a, t, st);
+  } else {
+    __syncthreads();  // every gather of this exchange is done
+    if (on) Rw::template pass_scatter<B>(a, L, t);
+    if constexpr (PS::BP != P) fwd_rest<P, E, PS::BP, TO_LDS>(a, L, t, st, tw, on);
+  }
+}
+
+// Inverse passes undoing forward passes B, B*R, ..., P.  The first one reads
+// the natural packed row through ld (global) or, when FROM_LDS, from L[0..P).
+// On return L holds the size-B spectra in layout B, synchronised.
+template <int P, int E, int B, bool FROM_LDS, class Ld, class TW>
+__device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld, const TW& tw, bool on = true) {
+  using Rw = Row<P, E>;
+  using PS = typename Rw::template Pass<B>;
+  auto from_lds = [L](int v, int c) { return L[v + c]; };
+  if constexpr (PS::BP == P) {
+    if constexpr (FROM_LDS) {
+      if (on) Rw::template inv_pass<B>(a, from_lds, t, tw);
+      __syncthreads();
+    } else {
+      if (on) Rw::template inv_pass<B>(a, ld, t, tw);
+    }
+  } else {
+    inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld, tw, on);
+    if (on) Rw::template inv_pass<B>(a, from_lds, t, tw);
+    __syncthreads();  // every gather of this exchange is done
+  }
+  if (on) Rw::template inv_scatter<B>(a, L, t);
+  __syncthreads();
+}
+
+// Inverse passes below the first one: on entry L holds spectra of size Bout in
+// layout Bout (synchronised); on return it holds the size-E spectra in layout E.
+template <int P, int E, int Bout, class TW>
+__device__ __forceinline__ void inv_down(float (&a)[E], float* L, int t, const TW& tw) {
+  if constexpr (Bout > E) {
+    using Rw = Row<P, E>;
+    constexpr int B = Rw::pass_in_for(Bout);
+    Rw::template inv_pass<B>(a, [L](int v, int c) { return L[v + c]; }, t, tw);
+    __syncthreads();  // every gather of this exchange is done
+    Rw::template inv_scatter<B>(a, L, t);
+    __syncthreads();
+    inv_down<P, E, B>(a, L, t, tw);
+  }
+}
+
+// Forward transform of one row into L[0..P) (natural packed order).
+// ld(var, cst) returns element var + cst (var = t, cst = T*s).  No barrier
+// after the final write.  Every thread of the workgroup must call it.
+// tw: the row's forward twiddles (Row<P, E>::FwdTws, loaded once by the caller).
+template <int P, class Ld, class TW>
+__device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW& tw, bool on = true) {
+  constexpr int E = elems_per_thread(P);
+  using Rw = Row<P, E>;
+  float a[E];
+  if (on) Rw::fwd_pass0(a, ld, t);
+  if constexpr (P == E) {
+    if (on) {
+#pragma unroll
+      for (int s = 0; s < P; ++s) L[s] = a[s];
+    }
+  } else {
+    if (on) Rw::fwd_pass0_scatter(a, L, t);
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw, on);
+  }
+}
+
+// The same from values already loaded (raw[s] = element t + T*s, widened by
+// widen): used where the loads were issued ahead of time.
+template <int P, class V, class Wd, class TW>
+__device__ __forceinline__ void row_fwd_raw_to_lds(const V (&raw)[elems_per_thread(P)], Wd widen, float* L, int t,
+                                                   const TW& tw, bool on = true) {
+  constexpr int E = elems_per_thread(P);
+  using Rw = Row<P, E>;
+  float a[E];
+  if (on) Rw::fwd_pass0_from(a, raw, widen);
+  if constexpr (P == E) {
+    if (on) {
+#pragma unroll
+      for (int s = 0; s < P; ++s) L[s] = a[s];
+    }
+  } else {
+    if (on) Rw::fwd_pass0_scatter(a, L, t);
+    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw, on);
+  }
+}
+
+// Inverse transform of the natural packed row in L[0..P) (the caller has
+// synchronised after writing it); st(var, cst, v) stores element var + cst.
+// L is used as exchange space; no barrier after the last read of L.
+// Every thread of the workgroup must call it.
+// tw: the row's inverse twiddles (Row<P, E>::InvTws, loaded once by the caller).
+template <int P, class St, class TW>
+__device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float scale, const TW& tw, bool on = true) {
+  constexpr int E = elems_per_thread(P);
+  using Rw = Row<P, E>;
+  float a[E];
+  if constexpr (P == E) {
+    if (on) {
+#pragma unroll
+      for (int s = 0; s < P; ++s) a[s] = L[s];
+      small_inv<P, 1>(a);
+      constexpr int LP = ilog2(P);
+#pragma unroll
+      for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
+    }
+  } else {
+    inv_rest<P, E, E, true>(a, L, t, [](int, int) { return 0.0f; }, tw, on);
+    if (on) Rw::inv_pass0_store(a, L, t, scale, st);
+  }
+}
+
 // Standalone kernels whose rows are short: a wavefront access of one row
 // covers T = P/16 consecutive elements, 16 to 64 bytes for 32 <= p <= 256.
 // The rows of a workgroup's group are contiguous, so they move between HBM
@@ -190,131 +315,6 @@ __device__ __forceinline__ void inv_block_loop(typename Io::T* __restrict__ data
     g += G;
     if (g >= ngroups) return;
     __syncthreads();  // the stores' LDS reads are done before the next group lands
-  }
-}
-
-// Forward passes with input spectra of size B and all later ones.  The last
-// pass either stores the natural packed row through st (global) or, when
-// TO_LDS, scatters it to L[0..P) (layout P is the natural order).
-// on = false (uniform per wavefront): the wave only takes part in the
-// barriers (a wave whose rows are all padding skips their arithmetic).
-template <int P, int E, int B, bool TO_LDS, class St, class TW>
-__device__ __forceinline__ void fwd_rest(float (&a)[E], float* L, int t, St st, const TW& tw, bool on = true) {
-  using Rw = Row<P, E>;
-  using PS = typename Rw::template Pass<B>;
-  __syncthreads();  // the previous pass's scatter is visible
-  if (on) Rw::template fwd_pass<B>(a, L, t, tw);
-  if constexpr (PS::BP == P && !TO_LDS) {
-    if (on) Rw::template last_store<B>(a, t, st);
-  } else {
-    __syncthreads();  // every gather of this exchange is done
-    if (on) Rw::template pass_scatter<B>(a, L, t);
-    if constexpr (PS::BP != P) fwd_rest<P, E, PS::BP, TO_LDS>(a, L, t, st, tw, on);
-  }
-}
-
-// Inverse passes undoing forward passes B, B*R, ..., P.  The first one reads
-// the natural packed row through ld (global) or, when FROM_LDS, from L[0..P).
-// On return L holds the size-B spectra in layout B, synchronised.
-template <int P, int E, int B, bool FROM_LDS, class Ld, class TW>
-__device__ __forceinline__ void inv_rest(float (&a)[E], float* L, int t, Ld ld, const TW& tw, bool on = true) {
-  using Rw = Row<P, E>;
-  using PS = typename Rw::template Pass<B>;
-  auto from_lds = [L](int v, int c) { return L[v + c]; };
-  if constexpr (PS::BP == P) {
-    if constexpr (FROM_LDS) {
-      if (on) Rw::template inv_pass<B>(a, from_lds, t, tw);
-      __syncthreads();
-    } else {
-      if (on) Rw::template inv_pass<B>(a, ld, t, tw);
-    }
-  } else {
-    inv_rest<P, E, PS::BP, FROM_LDS>(a, L, t, ld, tw, on);
-    if (on) Rw::template inv_pass<B>(a, from_lds, t, tw);
-    __syncthreads();  // every gather of this exchange is done
-  }
-  if (on) Rw::template inv_scatter<B>(a, L, t);
-  __syncthreads();
-}
-
-// Inverse passes below the first one: on entry L holds spectra of size Bout in
-// layout Bout (synchronised); on return it holds the size-E spectra in layout E.
-template <int P, int E, int Bout, class TW>
-__device__ __forceinline__ void inv_down(float (&a)[E], float* L, int t, const TW& tw) {
-  if constexpr (Bout > E) {
-    using Rw = Row<P, E>;
-    constexpr int B = Rw::pass_in_for(Bout);
-    Rw::template inv_pass<B>(a, [L](int v, int c) { return L[v + c]; }, t, tw);
-    __syncthreads();  // every gather of this exchange is done
-    Rw::template inv_scatter<B>(a, L, t);
-    __syncthreads();
-    inv_down<P, E, B>(a, L, t, tw);
-  }
-}
-
-// Forward transform of one row into L[0..P) (natural packed order).
-// ld(var, cst) returns element var + cst (var = t, cst = T*s).  No barrier
-// after the final write.  Every thread of the workgroup must call it.
-// tw: the row's forward twiddles (Row<P, E>::FwdTws, loaded once by the caller).
-template <int P, class Ld, class TW>
-__device__ __forceinline__ void row_fwd_to_lds(Ld ld, float* L, int t, const TW& tw, bool on = true) {
-  constexpr int E = elems_per_thread(P);
-  using Rw = Row<P, E>;
-  float a[E];
-  if (on) Rw::fwd_pass0(a, ld, t);
-  if constexpr (P == E) {
-    if (on) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) L[s] = a[s];
-    }
-  } else {
-    if (on) Rw::fwd_pass0_scatter(a, L, t);
-    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw, on);
-  }
-}
-
-// The same from values already loaded (raw[s] = element t + T*s, widened by
-// widen): used where the loads were issued ahead of time.
-template <int P, class V, class Wd, class TW>
-__device__ __forceinline__ void row_fwd_raw_to_lds(const V (&raw)[elems_per_thread(P)], Wd widen, float* L, int t,
-                                                   const TW& tw, bool on = true) {
-  constexpr int E = elems_per_thread(P);
-  using Rw = Row<P, E>;
-  float a[E];
-  if (on) Rw::fwd_pass0_from(a, raw, widen);
-  if constexpr (P == E) {
-    if (on) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) L[s] = a[s];
-    }
-  } else {
-    if (on) Rw::fwd_pass0_scatter(a, L, t);
-    fwd_rest<P, E, E, true>(a, L, t, [](int, int, float) {}, tw, on);
-  }
-}
-
-// Inverse transform of the natural packed row in L[0..P) (the caller has
-// synchronised after writing it); st(var, cst, v) stores element var + cst.
-// L is used as exchange space; no barrier after the last read of L.
-// Every thread of the workgroup must call it.
-// tw: the row's inverse twiddles (Row<P, E>::InvTws, loaded once by the caller).
-template <int P, class St, class TW>
-__device__ __forceinline__ void row_inv_from_lds(float* L, St st, int t, float scale, const TW& tw, bool on = true) {
-  constexpr int E = elems_per_thread(P);
-  using Rw = Row<P, E>;
-  float a[E];
-  if constexpr (P == E) {
-    if (on) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) a[s] = L[s];
-      small_inv<P, 1>(a);
-      constexpr int LP = ilog2(P);
-#pragma unroll
-      for (int s = 0; s < P; ++s) st(0, s, a[bitrev(s, LP)] * scale);
-    }
-  } else {
-    inv_rest<P, E, E, true>(a, L, t, [](int, int) { return 0.0f; }, tw, on);
-    if (on) Rw::inv_pass0_store(a, L, t, scale, st);
   }
 }
 

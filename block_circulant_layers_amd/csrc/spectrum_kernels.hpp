@@ -12,6 +12,21 @@
 
 namespace rdfft {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// the storage value of v (rounded to nearest even for 16-bit rows)
+template <class Io>
+__device__ __forceinline__ typename Io::T to_storage(float v) {
+  if constexpr (sizeof(typename Io::T) == 4)
+    return v;
+  else
+    return Io::narrow(v);
+}
+
+// Every element is touched once per call, so the accesses are non-temporal
+// (measured: 4096x512 fp32 unpack 6.5 -> 5.7 us; 1024x4096 unpack 10.9 ->
+// 9.1 us, pack 10.2 -> 9.3 us).
+
 // One thread per bin f < p/2 of packed row r (lp = log2 p): bin f = (z[f],
 // z[p-f]) written as one (Re, Im) pair, so each wavefront writes a contiguous
 // run of pairs and reads an ascending and a descending run of the packed row;
@@ -26,13 +41,13 @@ __global__ void __launch_bounds__(256)
     const int64_t r = i >> (lp - 1);
     const int f = static_cast<int>(i & (h - 1));
     const typename Io::T* row = z + (r << lp);
-    float2* bins = reinterpret_cast<float2*>(spec + 2 * r * nb);
-    const float re = Io::load(row + f);
+    f32x2* bins = reinterpret_cast<f32x2*>(spec + 2 * r * nb);
+    const float re = Io::widen(__builtin_nontemporal_load(row + f));
     if (f == 0) {
-      bins[0] = make_float2(re, 0.0f);
-      bins[h] = make_float2(Io::load(row + h), 0.0f);
+      __builtin_nontemporal_store(f32x2{re, 0.0f}, bins);
+      __builtin_nontemporal_store(f32x2{Io::widen(__builtin_nontemporal_load(row + h)), 0.0f}, bins + h);
     } else {
-      bins[f] = make_float2(re, Io::load(row + (p - f)));
+      __builtin_nontemporal_store(f32x2{re, Io::widen(__builtin_nontemporal_load(row + (p - f)))}, bins + f);
     }
   }
 }
@@ -52,12 +67,12 @@ __global__ void __launch_bounds__(256)
     typename Io::T* row = z + (r << lp);
     const float* bins = spec + 2 * r * nb;
     if (f == 0) {
-      Io::store(row, bins[0]);
-      Io::store(row + h, bins[2 * h]);
+      __builtin_nontemporal_store(to_storage<Io>(__builtin_nontemporal_load(bins)), row);
+      __builtin_nontemporal_store(to_storage<Io>(__builtin_nontemporal_load(bins + 2 * h)), row + h);
     } else {
-      const float2 b = reinterpret_cast<const float2*>(bins)[f];
-      Io::store(row + f, b.x);
-      Io::store(row + (p - f), b.y);
+      const f32x2 b = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(bins) + f);
+      __builtin_nontemporal_store(to_storage<Io>(b.x), row + f);
+      __builtin_nontemporal_store(to_storage<Io>(b.y), row + (p - f));
     }
   }
 }

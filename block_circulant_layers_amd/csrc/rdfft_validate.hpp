@@ -25,6 +25,9 @@ inline bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 // largest element count any call accepts (keeps every byte offset in int64)
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// widest circulant activation row: the circulant kernels address a batch of
+// up to 16 token rows through one buffer resource with 32-bit byte offsets
+constexpr int64_t kMaxFeatures = int64_t(1) << 24;
 
 inline int check_rdfft(const void* data, int64_t rows, int64_t p, int dtype) {
   if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;
@@ -59,7 +62,7 @@ inline int check_rdfft2d(const void* data, int64_t n, int64_t h, int64_t w, int 
 inline int check_circulant_dims(int64_t batch, int64_t d_in, int64_t d_out, int64_t p) {
   if (!valid_len(p, 4096) || batch < 0) return RDFFT_ERR_SIZE;
   if (d_in <= 0 || d_out <= 0 || d_in % p != 0 || d_out % p != 0) return RDFFT_ERR_SHAPE;
-  if (d_in > kMaxElems || d_out > kMaxElems || batch > kMaxElems / d_in || batch > kMaxElems / d_out ||
+  if (d_in > kMaxFeatures || d_out > kMaxFeatures || batch > kMaxElems / d_in || batch > kMaxElems / d_out ||
       (d_in / p) > kMaxElems / d_out)
     return RDFFT_ERR_SIZE;
   return RDFFT_OK;

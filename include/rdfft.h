@@ -31,7 +31,8 @@
  *     explicit complex spectra are always float.
  *   - Supported lengths: transforms and spectrum utilities p = 2, 4, 8, ...,
  *     32768 (a row is staged in one workgroup's LDS; the pages stop at 4096);
- *     circulant blocks p = 2, 4, ..., 4096.
+ *     circulant blocks p = 2, 4, ..., 4096, with d_in and d_out at most 2^24
+ *     (RDFFT_ERR_SIZE beyond).
  *   - Non-finite inputs are propagated, not checked.
  */
 #ifndef RDFFT_H

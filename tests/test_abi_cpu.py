@@ -92,6 +92,10 @@ def test_circulant_fwd_validation(L):
     assert f(A, C_, B_, 2, 64, 64, 12, F32, None) == SIZE
     assert f(A, C_, B_, 2, 64, 64, 8192, F32, None) == SIZE
     assert f(A, C_, B_, -1, 64, 64, 16, F32, None) == SIZE
+    # activation rows wider than 2^24 features, and a weight grid past 2^40 elements
+    assert f(A, C_, B_, 2, 1 << 25, 64, 16, F32, None) == SIZE
+    assert f(A, C_, B_, 2, 64, 1 << 25, 16, BF16, None) == SIZE
+    assert f(A, C_, B_, 2, 1 << 24, 1 << 24, 16, F32, None) == SIZE
     assert f(A, C_, B_, 2, 60, 64, 16, F32, None) == SHAPE
     assert f(A, C_, B_, 2, 64, 72, 16, F32, None) == SHAPE
     assert f(A, C_, B_, 2, 0, 64, 16, F32, None) == SHAPE
@@ -112,6 +116,7 @@ def test_circulant_bwd_validation(L):
     assert f(A, C_, B_, DX, None, 0, 64, 64, 16, F32, None) == OK  # empty batch, no dc to zero
     assert f(A, C_, B_, DX, DC, 2, 64, 48, 32, F32, None) == SHAPE
     assert f(A, C_, B_, DX, DC, 2, 64, 64, 5, F32, None) == SIZE
+    assert f(A, C_, B_, DX, DC, 2, 1 << 25, 64, 16, F32, None) == SIZE
     assert f(A, C_, B_, DX, DC, 2, 64, 64, 16, 3, None) == DTYPE
     assert f(A, C_, B_, ctypes.c_void_p(0x400004), DC, 2, 64, 64, 16, F32, None) == ALIGN
     # dx overlapping dy, dc overlapping c / x

@@ -39,8 +39,8 @@ def test_transform_graph_replays():
         assert torch.equal(buf, eager), i
 
 
-# p = 128: dx and dc in one launch; p = 4096: separate dx and dc kernels; p = 16:
-# the small-p kernels
+# p = 128 and 4096: dx and dc in one launch (at 4096 with a wider dx tile than
+# the forward's); p = 16: the small-p kernels
 @pytest.mark.parametrize("b,d,p", [(64, 1024, 128), (32, 4096, 4096), (24, 256, 16)])
 def test_circulant_graph_replays(b, d, p):
     x, _ = device_input((b, d), syn.WL_TEST, syn.T_X, 32, dtype="bf16")

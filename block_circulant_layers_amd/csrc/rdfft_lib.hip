@@ -183,8 +183,8 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
                               static_cast<size_t>(S::lds_bytes()), s>>>(
         static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k), int(q), tpw);
     st = launch_status();
-    if (st != RDFFT_OK) return st;
-    return launch_rdfft<P, F32Io, true>(dc, q * k, s);
+    if (st != RDFFT_OK || dc_time_domain(P, false)) return st;
+    return launch_rdfft<P, F32Io, true>(dc, q * k, s);  // dc holds packed spectra
   } else {
     return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s);
   }
@@ -221,7 +221,6 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
           int(gxx));
       st = launch_status();
     }
-    if (st == RDFFT_OK) st = launch_rdfft<P, F32Io, true>(dc, q * k, s);
     *status = st;
     return true;
   } else {

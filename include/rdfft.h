@@ -111,11 +111,13 @@ int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t
  *   dy  [batch, d_out]  dtype, read only
  *   dx  [batch, d_in]   dtype, overwritten; may be NULL to skip it
  *   dc  [q, k, p]       float, OVERWRITTEN (not accumulated) with the sum over
- *                       all tokens; may be NULL to skip it.  It serves as the
- *                       accumulator of the token sum in the packed spectral
- *                       domain and is transformed back in place, so the order
- *                       of the fp32 token sum is not fixed (results may differ
- *                       in the last bits from call to call).
+ *                       all tokens; may be NULL to skip it.  It is zeroed and
+ *                       then serves as the accumulator of the token sum:
+ *                       partial sums over token ranges are added atomically,
+ *                       transformed back first or (for some p) as packed
+ *                       spectra that an in-place inverse then transforms, so
+ *                       the order of the fp32 token sum is not fixed (results
+ *                       may differ in the last bits from call to call).
  * dx and dc must not both be NULL, and must not overlap each other or any
  * input.  When batch == 0, dc is set to zero (if given).
  */

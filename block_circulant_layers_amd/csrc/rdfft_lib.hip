@@ -199,7 +199,7 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
                            int64_t k, int64_t q, hipStream_t s, int* status) {
   if constexpr (bwd_fusable<P>()) {
     using S = TpShape<P, true>;
-    using D = DtpShape<P, true>;
+    using D = DtpShape<P>;
     if (q > S::CR || !S::fits(static_cast<int>(q)) || S::lds_bytes(static_cast<int>(q)) > kMaxLds ||
         k > 0x7fffffff)
       return false;

@@ -111,10 +111,13 @@ def test_dc_overwritten_and_optional_outputs():
 
 
 @pytest.mark.parametrize("batch,d,p,dtype", [(256, 4096, 128, "bf16"), (96, 2048, 512, "f32"), (512, 4096, 1024, "bf16"),
-                                            (40, 4096, 2048, "f16"), (64, 4096, 4096, "f32")])
+                                            (40, 4096, 2048, "f16"), (64, 4096, 4096, "f32"), (70, 1024, 64, "bf16"),
+                                            (45, 2048, 256, "f32")])
 def test_backward_single_outputs(batch, d, p, dtype):
     # dx alone and dc alone take other launches than the two together (one
-    # launch holds both where the row length allows): each against the oracle
+    # launch holds both where the row length allows; dc alone adds packed
+    # spectra and transforms dc back afterwards at p <= 128, time-domain sums
+    # from p = 256): each against the oracle
     q = k = d // p
     x, xr = device_input((batch, d), syn.WL_TEST, syn.T_X, p + 3, dtype=dtype)
     c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, p + 3, scale=1 / np.sqrt(d), dtype="f32")

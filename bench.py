@@ -2,17 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Headline step: 4096 rows of p = 512, fp32, forward then inverse rdFFT in
-place (one pass of the transform path over one batch).  Each step works on
-the next of NBUF distinct copies (>= 1 GiB in total) so the 256 MB last-level
-cache cannot hold the data between steps; every buffer is resident in HBM
-before the timed region starts.  `value` = algorithmic bytes (every row read
-once and written once, per transform) / wall time of the K steps.
+Headline step: 4096 rows of p = 512, fp32, one forward and one inverse rdFFT
+in place (one pass of the transform path over one batch).  Exactly W untimed
+and K timed steps run.  The batch rotates over NBUF distinct copies (1 GiB in
+total): step g transforms copy g mod NBUF forward and copy (g + NBUF/2) mod
+NBUF back, so no step reads what the 256 MB last-level cache still holds;
+every copy is resident in HBM before the timed region starts.  `value` =
+algorithmic bytes (every row read once and written once, per transform) /
+wall time of the K steps.
 
 The JSON line also carries
   roofline      the forward kernel: algorithmic bytes per launch / its mean
-                launch duration (HIP events around every launch in the timed
-                region, on the launch stream), against 8 TB/s HBM;
+                duration per launch in the timed region (HIP events around
+                each run of back-to-back forward launches, on the launch
+                stream), against 8 TB/s HBM; beside it the average duration
+                of the same dispatches in the committed kernel-trace summary;
   cpu_baseline  the fp64 oracle (numpy) on all host cores (up to 16) and on
                 one thread, each on a bounded sample of the same workload, in
                 the same unit;
@@ -83,6 +87,25 @@ def recorded_traffic(kernel_key: str):
     return None
 
 
+def recorded_trace_ms(kernel: str):
+    """The headline kernel's average duration (ms) over the timed region's
+    dispatches in the committed kernel-trace summary of bench.py, or None when
+    that summary was taken on other transform sources."""
+    path = os.path.join(PROFILES, "kernel_trace_bench_default.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", txt)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    want = kernel.replace(" ", "")
+    for line in txt.split("timed region's dispatches only")[-1].splitlines():
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and cells[0].replace(" ", "") == want:
+            return float(cells[2]) * 1e-3
+    return None
+
+
 class Timer:
     """Events on the stream the kernels are launched on (torch's current stream)."""
 
@@ -97,6 +120,26 @@ class Timer:
         self.b.record()
         self.b.synchronize()
         return self.a.elapsed_time(self.b)
+
+
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_gpu(ms: float) -> None:
+    """Keep the current stream busy for about ``ms`` milliseconds with torch's
+    bounded spin kernel, so that the host queues the launches that follow
+    before the GPU reaches them: events recorded after it then time GPU
+    execution, not the host's launch rate."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        b.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
 
 
 # ---------------------------------------------------------------------------
@@ -121,51 +164,90 @@ def _replayer(fn, eager):
     return _graph(fn).replay
 
 
+def step_runs(g0, n, chunk):
+    """Split the global steps [g0, g0 + n) into runs that never cross a
+    multiple of ``chunk``: [(first step, length), ...]."""
+    runs, g = [], g0
+    while g < g0 + n:
+        m = min(g0 + n, (g // chunk + 1) * chunk) - g
+        runs.append((g, m))
+        g += m
+    return runs
+
+
 def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
-    """Steps of (forward, inverse) in place on one batch, the batch rotating
-    over nbuf distinct copies.  Launches are replayed from two HIP graphs: all
-    nbuf forwards, then all nbuf inverses (each buffer gets forward then
-    inverse, as in a step).  Events around the forward graph give the forward
-    kernel's mean launch duration."""
+    """Exactly ``warmup`` untimed and ``steps`` timed steps of one forward and
+    one inverse transform in place, each on a 1 GiB rotation of nbuf copies of
+    one batch: step g runs the forward on buffer g mod nbuf and the inverse on
+    buffer (g + nbuf/2) mod nbuf, so a buffer's forward and its inverse are
+    nbuf/2 steps (1 GiB of traffic) apart and neither reads from a cache.
+    Steps are launched in runs of up to nbuf/2 from HIP graphs (cached per run
+    position, all captured before the timed region): the run's forwards, then
+    its inverses, with events between them, giving the mean duration of a
+    forward and of an inverse launch in the timed region.  A bounded spin
+    kernel holds the GPU while the host queues the timed runs, so the events
+    time back-to-back GPU execution."""
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     eb = 4 if dtype == "f32" else 2
     nbytes = rows * p * eb
     nbuf = max(2, ROTATE_BYTES // nbytes)
+    nbuf -= nbuf % 2
+    half = nbuf // 2
+    chunk = half
     base = syn.torch_normal((rows, p), workload, syn.T_X, index, dtype=tdt)
     bufs = [base.clone() for _ in range(nbuf)]
-    g_fwd = _replayer(lambda: [bcl.rdfft_forward(b) for b in bufs], eager)
-    g_inv = _replayer(lambda: [bcl.rdfft_inverse(b) for b in bufs], eager)
-    reps_w = max(1, -(-warmup // nbuf))
-    reps = max(1, -(-steps // nbuf))
-    for _ in range(reps_w):
-        g_fwd()
-        g_inv()
+    graphs = {}
+
+    def run_fns(g, n):
+        key = (g % nbuf, n)
+        if key not in graphs:
+            fwd = lambda g=g, n=n: [bcl.rdfft_forward(bufs[(g + i) % nbuf]) for i in range(n)]  # noqa: E731
+            inv = lambda g=g, n=n: [bcl.rdfft_inverse(bufs[(g + half + i) % nbuf]) for i in range(n)]  # noqa: E731
+            graphs[key] = (_replayer(fwd, eager), _replayer(inv, eager))
+        return graphs[key]
+
+    # capture every run's graphs before anything is timed
+    warm_runs = step_runs(0, warmup, chunk)
+    timed_runs = step_runs(warmup, steps, chunk)
+    for g, n in warm_runs + timed_runs:
+        run_fns(g, n)
+    for g, n in warm_runs:
+        f, i = run_fns(g, n)
+        f()
+        i()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in timed_runs]
     tm = Timer()
     torch.cuda.synchronize()
+    hold_gpu(1.0 + 0.15 * len(timed_runs))  # the runs are queued before the GPU starts them
     tm.start()
-    for r in range(reps):
-        ev[r][0].record()
-        g_fwd()
-        ev[r][1].record()
-        g_inv()
-        ev[r][2].record()
+    for (g, n), e in zip(timed_runs, ev):
+        f, i = run_fns(g, n)
+        e[0].record()
+        f()
+        e[1].record()
+        i()
+        e[2].record()
     ms = tm.stop()
     torch.cuda.synchronize()
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / (reps * nbuf)
-    inv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / (reps * nbuf)
-    # every buffer has been through (reps + reps_w) round trips: still the input
-    drift = float((bufs[0].float() - base.float()).abs().max() / base.float().abs().max())
-    nsteps = reps * nbuf
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / max(1, steps)
+    inv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / max(1, steps)
+    # a buffer that has had as many forwards as inverses holds its input again
+    total = warmup + steps
+    drift = None
+    for b in range(nbuf):
+        nops = sum(1 for g in range(total) if g % nbuf == b) + sum(1 for g in range(total) if (g + half) % nbuf == b)
+        if nops % 2 == 0:
+            drift = float((bufs[b].float() - base.float()).abs().max() / base.float().abs().max())
+            break
     step_bytes = 2 * 2 * nbytes  # forward + inverse, each reads and writes every row once
-    del bufs, g_fwd, g_inv, base
+    del bufs, graphs, base
     torch.cuda.empty_cache()
     return {
-        "steps": nsteps,
-        "warmup": reps_w * nbuf,
-        "ms_per_step": ms / nsteps,
-        "gbs": step_bytes / (ms / nsteps) / 1e6,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms / max(1, steps),
+        "gbs": step_bytes / (ms / max(1, steps)) / 1e6,
         "bytes_per_launch": 2 * nbytes,
         "fwd_ms": fwd_ms,
         "inv_ms": inv_ms,
@@ -230,6 +312,61 @@ def bench_rdfft2d(h, w, steps, warmup):
     return {"fwd_ms": round(fwd, 5), "inv_ms": round(inv, 5),
             "fwd_gbs_algorithmic": round(2 * nbytes / (fwd * 1e-3) / 1e9, 1),
             "inv_gbs_algorithmic": round(2 * nbytes / (inv * 1e-3) / 1e9, 1)}
+
+
+def _stream_lib():
+    import ctypes
+
+    from block_circulant_layers_amd import build
+
+    if not os.path.exists(build.PROBE_LIB):
+        raise RuntimeError(f"{build.PROBE_LIB} is not built: run python -m block_circulant_layers_amd.build")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.stream_probe.restype = ctypes.c_int
+    lib.stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                 ctypes.c_void_p]
+    return lib
+
+
+def bench_stream(nbytes, launches=512):
+    """The in-place streaming pass of libstreamprobe.so (every float read once
+    and written back once, scaled by 1: an in-place transform's HBM traffic
+    with none of its arithmetic) over a 1 GiB rotation of nbytes buffers, for
+    both cache policies and a few grid sizes.  Reported per policy: the mean
+    time per launch of graph-replayed back-to-back launches, best grid."""
+    lib = _stream_lib()
+    n = nbytes // 4
+    nbuf = max(2, ROTATE_BYTES // nbytes)
+    bufs = [torch.zeros(n, device="cuda") for _ in range(nbuf)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    chunks = -(-n // 4096)
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    out = {}
+    for policy, name in ((0, "default_policy"), (1, "non_temporal")):
+        best = None
+        for grid in sorted({min(chunks, cus * r) for r in (2, 4, 8)} | {chunks}):
+            def launch_all(grid=grid, policy=policy):
+                for b in bufs:
+                    if lib.stream_probe(b.data_ptr(), n, grid, policy, 1.0, stream()) != 0:
+                        raise RuntimeError("stream_probe failed")
+            g = _graph(launch_all)
+            g.replay()
+            reps = max(1, -(-launches // nbuf))
+            tm = Timer()
+            torch.cuda.synchronize()
+            hold_gpu(1.0)
+            tm.start()
+            for _ in range(reps):
+                g.replay()
+            us = tm.stop() * 1e3 / (reps * nbuf)
+            del g
+            if best is None or us < best["us_per_launch"]:
+                best = {"grid": grid, "us_per_launch": round(us, 3),
+                        "pct_hbm_peak": round(100 * 2 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
+        out[name] = best
+    del bufs
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_copy(nbytes, steps, warmup):
@@ -411,6 +548,7 @@ def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
     reps = max(1, -(-steps // nrot))
     tm = Timer()
     torch.cuda.synchronize()
+    hold_gpu(1.0)
     tm.start()
     for _ in range(reps):
         g.replay()
@@ -445,6 +583,7 @@ def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=102
         g.replay()
     tm = Timer()
     torch.cuda.synchronize()
+    hold_gpu(1.0)
     tm.start()
     for _ in range(steps):
         g.replay()
@@ -478,6 +617,54 @@ def profile_circulant(reps=3):
         log(f"profiled circulant {name}: B={batch} D={d} p={p}, {reps} x (forward, backward)")
 
 
+def trace_summary(trace_dir: str, steps: int, warmup: int, command: str) -> str:
+    """Markdown summary of a ``rocprofv3 --kernel-trace --stats`` run of this
+    script (csv output in ``trace_dir``): every kernel of this library by total
+    time, and the headline forward kernel's average over the dispatches of the
+    timed region alone (its dispatches warmup .. warmup + steps - 1 in launch
+    order), the duration bench.py's roofline is to agree with."""
+    import csv
+    import glob
+
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {trace_dir}")
+    short = lambda n: re.sub(r"rdfft::|\(anonymous namespace\)::|^void ", "", n.split("(")[0])  # noqa: E731
+    rows = [r for r in csv.DictReader(open(stats[0])) if "rdfft::" in r["Name"] or "stream_inplace" in r["Name"]]
+    lines = [
+        "# Kernel trace: bench.py",
+        "",
+        f"source_hash: {kernel_source_hash()}",
+        "(hash of rdfft_device.hpp, rdfft_kernels.hpp and gen_twiddles.py as traced; bench.py reports",
+        "`roofline.kernel_ms_traced` only while the current sources hash to this value)",
+        "",
+        "Command (repository root, one MI355X, libraries built with `python -m block_circulant_layers_amd.build`):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "This library's kernels (and the streaming reference pass), by total time; durations in microseconds,",
+        "the tracer's start-to-end of each dispatch:",
+        "",
+        "| kernel | calls | avg us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    head = [r for r in csv.DictReader(open(trace[0])) if "rdfft_fwd_kernel<512, rdfft::F32Io>" in r["Kernel_Name"]]
+    head.sort(key=lambda r: int(r["Start_Timestamp"]))
+    timed = head[warmup: warmup + steps]
+    if timed:
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        lines += ["", "Headline forward kernel, the timed region's dispatches only:", "",
+                  "| kernel | timed dispatches | avg us | min us | max us |", "|---|---|---|---|---|",
+                  f"| rdfft_fwd_kernel<512, F32Io> | {len(d)} | {np.mean(d):.2f} | {min(d):.2f} | {max(d):.2f} |"]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,7 +682,15 @@ def main():
                     help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
     ap.add_argument("--profile-circulant", action="store_true",
                     help="only launch the circulant workloads eagerly, for counter collection, and exit")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write the markdown summary of a rocprofv3 kernel trace of this script (csv files under "
+                         "DIR, taken with the same --steps/--warmup) to stdout and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.trace_summary:
+        cmd = (f"rocprofv3 --kernel-trace --stats -d {args.trace_summary} -o ktrace --output-format csv -- "
+               f"python3 -u bench.py --steps {args.steps} --warmup {args.warmup}")
+        sys.stdout.write(trace_summary(args.trace_summary, args.steps, args.warmup, cmd))
+        return
     if args.gpus != 1:
         print(
             f"bench.py measures one GPU only (asked for {args.gpus}); the transform rows and the layer's "
@@ -523,7 +718,9 @@ def main():
     log(f"headline: rdfft {rows}x{p} {dt} fwd+inv, warmup {args.warmup}, steps {args.steps}")
     wl = syn.WL_RDFFT_512 if (rows, p) == (4096, 512) else syn.WL_RDFFT_LARGE
     h = bench_rdfft(rows, p, dt, args.steps, args.warmup, wl, eager=args.eager)
+    kname = f"rdfft_fwd_kernel<{p}, {IO_NAME[dt]}>"
     achieved = h["bytes_per_launch"] / (h["fwd_ms"] * 1e-3) / 1e9
+    traced = recorded_trace_ms(kname)
     out = {
         "metric": METRIC,
         "value": round(h["gbs"], 2),
@@ -542,7 +739,7 @@ def main():
             "rows": rows,
             "p": p,
             "rotating_buffers": h["nbuf"],
-            "launch": "eager launches" if args.eager else "HIP graph replays of the rotating set",
+            "launch": "eager launches" if args.eager else "HIP graph replays, runs of up to rotating_buffers / 2 steps",
             "roundtrip_drift": h["roundtrip_drift"],
             "pct_hbm_peak": round(100 * h["gbs"] / HBM_PEAK_GBS, 2),
         },
@@ -552,9 +749,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(f"rdfft_fwd_kernel<{p}, {IO_NAME[dt]}> {rows}x{p}"),
-            "kernel": f"rdfft_fwd_kernel<{p}, {IO_NAME[dt]}>",
+            "traffic": recorded_traffic(f"{kname} {rows}x{p}"),
+            "kernel": kname,
             "kernel_ms": round(h["fwd_ms"], 6),
+            "duration": "mean per forward launch in the timed region (HIP events around each run's graph of "
+                        "back-to-back forward launches, on the launch stream)",
+            "kernel_ms_traced": traced,
+            "frac_traced": None if traced is None else round(h["bytes_per_launch"] / (traced * 1e-3) / 1e9
+                                                              / HBM_PEAK_GBS, 4),
             "inverse_kernel_ms": round(h["inv_ms"], 6),
         },
     }
@@ -563,28 +765,18 @@ def main():
         out["cpu_baseline"] = cpu_baseline_rdfft(rows, p, args.cpu_seconds)
     if not args.no_extra:
         extra = {}
-        for (r, pp, dt) in ((4096, 4096, "f32"), (4096, 4096, "bf16"), (16384, 128, "f32"), (16384, 128, "bf16")):
-            log(f"extra: rdfft {r}x{pp} {dt}")
-            e = bench_rdfft(r, pp, dt, max(256, args.steps // 4), max(32, args.warmup // 4), syn.WL_RDFFT_LARGE)
-            ach = e["bytes_per_launch"] / (e["fwd_ms"] * 1e-3) / 1e9
-            extra[f"rdfft_{r}x{pp}_{dt}"] = {
-                "gbs_fwd_plus_inv": round(e["gbs"], 1),
-                "pct_hbm_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 2),
-                "fwd_kernel_gbs": round(ach, 1),
-                "fwd_kernel_ms": round(e["fwd_ms"], 5),
-                "inv_kernel_ms": round(e["inv_ms"], 5),
-            }
-        for (r, pp, dt) in ((4096, 1024, "f32"), (4096, 2048, "f32"), (16384, 1024, "f32"), (4096, 4096, "f16"),
+        for (r, pp, dt) in ((4096, 4096, "f32"), (4096, 4096, "bf16"), (16384, 128, "f32"), (16384, 128, "bf16"),
+                            (4096, 1024, "f32"), (4096, 2048, "f32"), (16384, 1024, "f32"), (4096, 4096, "f16"),
                             (2048, 8192, "f32"), (512, 32768, "f32")):
             log(f"extra: rdfft {r}x{pp} {dt}")
             e = bench_rdfft(r, pp, dt, max(256, args.steps // 4), max(32, args.warmup // 4), syn.WL_RDFFT_LARGE)
-            ach = e["bytes_per_launch"] / (e["fwd_ms"] * 1e-3) / 1e9
             extra[f"rdfft_{r}x{pp}_{dt}"] = {
                 "gbs_fwd_plus_inv": round(e["gbs"], 1),
                 "pct_hbm_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 2),
-                "fwd_kernel_gbs": round(ach, 1),
                 "fwd_kernel_ms": round(e["fwd_ms"], 5),
                 "inv_kernel_ms": round(e["inv_ms"], 5),
+                "fwd_kernel_pct_hbm_peak": round(100 * e["bytes_per_launch"] / (e["fwd_ms"] * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBS, 2),
             }
         log("extra: 2D 4096x4096 f32")
         extra["rdfft2d_4096x4096_f32"] = bench_rdfft2d(4096, 4096, 256, 32)
@@ -593,6 +785,8 @@ def main():
         for mib in (8, 64):
             log(f"extra: device copy {mib} MiB")
             extra[f"copy_ceiling_{mib}mib"] = bench_copy(mib << 20, 1024, 128)
+            log(f"extra: in-place streaming pass {mib} MiB")
+            extra[f"stream_ceiling_{mib}mib"] = bench_stream(mib << 20)
         for pp in (128, 512, 4096):
             log(f"extra: circulant layer D=4096 B=256 p={pp}")
             extra[f"circulant_d4096_b256_p{pp}_bf16"] = bench_circ_layer(256, 4096, pp, 256, 32)

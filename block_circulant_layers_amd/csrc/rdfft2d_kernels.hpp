@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(ColShape<H>::NT) col_kernel(typename Io::T* __
   using S = ColShape<H>;
   constexpr int E = S::E, T = S::T, CS = S::CS, CL = S::CL, CP = S::CP, NT = S::NT;
   using Rw = Row<H, E>;
-  extern __shared__ float lds[];
+  RDFFT_DYNAMIC_LDS(lds);
   const int tid = threadIdx.x;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int c0 = static_cast<int>(tile % ntiles) * CL;

@@ -47,6 +47,13 @@
 
 #include <type_traits>
 
+// The workgroup's LDS block whose size the launch gives (dynamic shared
+// memory).  A host build of these headers that runs the kernels on CPU
+// threads (the LDS schedule checker among the tests) defines it beforehand.
+#ifndef RDFFT_DYNAMIC_LDS
+#define RDFFT_DYNAMIC_LDS(name) extern __shared__ float name[]
+#endif
+
 namespace rdfft {
 
 struct Tw {
@@ -175,6 +182,11 @@ RDFFT_PASS_TW(8192, 2)
 RDFFT_PASS_TW(8192, 4)
 RDFFT_PASS_TW(32, 16)
 RDFFT_PASS_TW(512, 16)
+RDFFT_PASS_TW(8, 4)
+RDFFT_PASS_TW(32, 4)
+RDFFT_PASS_TW(512, 2)
+RDFFT_PASS_TW(512, 4)
+RDFFT_PASS_TW(2048, 2)
 #undef RDFFT_PASS_TW
 
 // the R-1 twiddles of an item, read as R/2 aligned 16-byte loads

@@ -325,19 +325,14 @@ __device__ __forceinline__ void inv_block_loop(typename Io::T* __restrict__ data
 // of different groups overlap.  The twiddles depend only on the thread and
 // stay in registers across the loop.
 // ---------------------------------------------------------------------------
-template <int P, class Io>
-__global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io>())),
-                                  wg_per_cu(P, is_f32_io<Io>()) *
-                                      wg_threads(P, standalone_elems(P, is_f32_io<Io>())) / 256)
-    rdfft_fwd_kernel(typename Io::T* __restrict__ data, int64_t rows) {
-  constexpr int E = standalone_elems(P, is_f32_io<Io>());
+template <int P, class Io, int E = standalone_elems(P, is_f32_io<Io>()), int NT = wg_threads(P, E)>
+__device__ __forceinline__ void rdfft_fwd_body(typename Io::T* __restrict__ data, int64_t rows) {
   using Rw = Row<P, E>;
   constexpr int T = Rw::T;
-  constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / T;
   constexpr int SEG = cmin(T, 64) * static_cast<int>(sizeof(typename Io::T));  // bytes per row per wave access
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
-  if constexpr (block_io(P, sizeof(typename Io::T))) {
+  if constexpr (block_io(P, sizeof(typename Io::T)) && E == elems_per_thread(P)) {
     fwd_block_loop<P, Io, NT>(data, rows, lds);
     return;
   }
@@ -360,7 +355,7 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
   load(raw, g);
   typename Rw::FwdTws tw;
   tw.load(t);
-  float* L = lds + rl * Rw::LDS;
+  float* L = (P == E) ? lds : lds + rl * Rw::LDS;  // rows of P == E never touch LDS
   while (true) {
     float a[E];
     Rw::fwd_pass0_from(a, raw, [](typename Io::T v) { return Io::widen(v); });
@@ -387,20 +382,15 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
   }
 }
 
-template <int P, class Io>
-__global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io>())),
-                                  wg_per_cu(P, is_f32_io<Io>()) *
-                                      wg_threads(P, standalone_elems(P, is_f32_io<Io>())) / 256)
-    rdfft_inv_kernel(typename Io::T* __restrict__ data, int64_t rows) {
-  constexpr int E = standalone_elems(P, is_f32_io<Io>());
+template <int P, class Io, int E = standalone_elems(P, is_f32_io<Io>()), int NT = wg_threads(P, E)>
+__device__ __forceinline__ void rdfft_inv_body(typename Io::T* __restrict__ data, int64_t rows) {
   using Rw = Row<P, E>;
   constexpr int T = Rw::T;
-  constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / T;
   constexpr int SEG = cmin(T, 64) * static_cast<int>(sizeof(typename Io::T));  // bytes per row per wave access
   constexpr float scale = 1.0f / static_cast<float>(P);
   __shared__ float lds[(P == E) ? 1 : ROWS * Rw::LDS];
-  if constexpr (block_io(P, sizeof(typename Io::T))) {
+  if constexpr (block_io(P, sizeof(typename Io::T)) && E == elems_per_thread(P)) {
     inv_block_loop<P, Io, NT>(data, rows, lds);
     return;
   }
@@ -430,7 +420,7 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
   load(raw, g);
   typename Rw::InvTws tw;
   tw.load(t);
-  float* L = lds + rl * Rw::LDS;
+  float* L = (P == E) ? lds : lds + rl * Rw::LDS;  // rows of P == E never touch LDS
   auto widen = [](typename Io::T v) { return Io::widen(v); };
   while (true) {
     float a[E];
@@ -462,6 +452,22 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
   }
 }
 
+template <int P, class Io>
+__global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io>())),
+                                  wg_per_cu(P, is_f32_io<Io>()) *
+                                      wg_threads(P, standalone_elems(P, is_f32_io<Io>())) / 256)
+    rdfft_fwd_kernel(typename Io::T* __restrict__ data, int64_t rows) {
+  rdfft_fwd_body<P, Io>(data, rows);
+}
+
+template <int P, class Io>
+__global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io>())),
+                                  wg_per_cu(P, is_f32_io<Io>()) *
+                                      wg_threads(P, standalone_elems(P, is_f32_io<Io>())) / 256)
+    rdfft_inv_kernel(typename Io::T* __restrict__ data, int64_t rows) {
+  rdfft_inv_body<P, Io>(data, rows);
+}
+
 // ---------------------------------------------------------------------------
 // rows longer than 8192 (16384 and 32768; fp32 32768 = 128 KB, in one CU's
 // LDS; rows of 8192 run in the standalone kernels above, measured 2048x8192
@@ -480,7 +486,7 @@ __global__ void __launch_bounds__(P / long_elems(P)) rdfft_fwd_long_kernel(typen
   using Rw = Row<P, E>;
   constexpr int T = Rw::T;
   constexpr int SEG = 64 * static_cast<int>(sizeof(typename Io::T));
-  extern __shared__ float lds[];
+  RDFFT_DYNAMIC_LDS(lds);
   const int t = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + static_cast<int64_t>(blockIdx.x) * P, P);
   const typename Rw::GlobalTws tw;
@@ -503,7 +509,7 @@ __global__ void __launch_bounds__(P / long_elems(P)) rdfft_inv_long_kernel(typen
   constexpr int E = long_elems(P);
   using Rw = Row<P, E>;
   constexpr int SEG = 64 * static_cast<int>(sizeof(typename Io::T));
-  extern __shared__ float lds[];
+  RDFFT_DYNAMIC_LDS(lds);
   const int t = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + static_cast<int64_t>(blockIdx.x) * P, P);
   const typename Rw::GlobalTws tw;

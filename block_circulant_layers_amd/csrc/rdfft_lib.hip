@@ -37,9 +37,9 @@ int launch_rdfft(void* data, int64_t rows, hipStream_t stream) {
   const int64_t grid = groups < resident ? groups : resident;
   auto* d = static_cast<typename Io::T*>(data);
   if (INV)
-    rdfft_inv_kernel<P, Io><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(d, rows);
+    hipLaunchKernelGGL((rdfft_inv_kernel<P, Io>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream, d, rows);
   else
-    rdfft_fwd_kernel<P, Io><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(d, rows);
+    hipLaunchKernelGGL((rdfft_fwd_kernel<P, Io>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream, d, rows);
   return launch_status();
 }
 
@@ -50,9 +50,9 @@ int launch_rdfft_long(void* data, int64_t rows, hipStream_t stream) {
   if (rows > 0x7fffffff) return RDFFT_ERR_SIZE;
   auto* d = static_cast<typename Io::T*>(data);
   if (INV)
-    rdfft_inv_long_kernel<P, Io><<<dim3(static_cast<unsigned>(rows)), dim3(P / E), lds, stream>>>(d);
+    hipLaunchKernelGGL((rdfft_inv_long_kernel<P, Io>), dim3(static_cast<unsigned>(rows)), dim3(P / E), lds, stream, d);
   else
-    rdfft_fwd_long_kernel<P, Io><<<dim3(static_cast<unsigned>(rows)), dim3(P / E), lds, stream>>>(d);
+    hipLaunchKernelGGL((rdfft_fwd_long_kernel<P, Io>), dim3(static_cast<unsigned>(rows)), dim3(P / E), lds, stream, d);
   return launch_status();
 }
 
@@ -92,15 +92,15 @@ int launch_circ_mm(const void* in, const float* c, void* out, int64_t batch, int
   const auto* pi = static_cast<const typename Io::T*>(in);
   auto* po = static_cast<typename Io::T*>(out);
   if (trans)
-    circ_mm_kernel<P, true, Io><<<grid, dim3(K.nt), 0, s>>>(pi, c, po, batch, int(nin), int(nout));
+    hipLaunchKernelGGL((circ_mm_kernel<P, true, Io>), grid, dim3(K.nt), 0, s, pi, c, po, batch, int(nin), int(nout));
   else
-    circ_mm_kernel<P, false, Io><<<grid, dim3(K.nt), 0, s>>>(pi, c, po, batch, int(nin), int(nout));
+    hipLaunchKernelGGL((circ_mm_kernel<P, false, Io>), grid, dim3(K.nt), 0, s, pi, c, po, batch, int(nin), int(nout));
   return launch_status();
 }
 
 int launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
-  fill_zero_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(p, n);
+  hipLaunchKernelGGL((fill_zero_kernel), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n);
   return launch_status();
 }
 
@@ -117,8 +117,9 @@ int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int6
   if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
   int st = launch_fill_zero(dc, q * k * P, s);
   if (st != RDFFT_OK) return st;
-  circ_dc_kernel<P, Io><<<dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(K.nt), 0, s>>>(
-      static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k), int(q), tpw);
+  hipLaunchKernelGGL((circ_dc_kernel<P, Io>), dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(K.nt), 0, s,
+                     static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k),
+                     int(q), tpw);
   st = launch_status();
   if (st != RDFFT_OK) return st;
   return launch_rdfft<P, F32Io, true>(dc, q * k, s);
@@ -155,11 +156,11 @@ int launch_circ_product(const void* in, const float* c, void* out, int64_t batch
       auto* po = static_cast<typename Io::T*>(out);
       if (!zero) nzero = 0;
       if (trans)
-        circ_tp_kernel<P, true, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw, zero,
-                                                                    nzero);
+        hipLaunchKernelGGL((circ_tp_kernel<P, true, Io>), grid, dim3(S::K.nt), lds, s, pi, c, po, batch, int(nin),
+                           int(nout), tpw, zero, nzero);
       else
-        circ_tp_kernel<P, false, Io><<<grid, dim3(S::K.nt), lds, s>>>(pi, c, po, batch, int(nin), int(nout), tpw,
-                                                                     zero, nzero);
+        hipLaunchKernelGGL((circ_tp_kernel<P, false, Io>), grid, dim3(S::K.nt), lds, s, pi, c, po, batch, int(nin),
+                           int(nout), tpw, zero, nzero);
       if (zeroed) *zeroed = nzero > 0;
       return launch_status();
     }
@@ -179,9 +180,9 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
     if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
     int st = zeroed ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);
     if (st != RDFFT_OK) return st;
-    circ_dctp_kernel<P, Io><<<dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(S::K.nt),
-                              static_cast<size_t>(S::lds_bytes()), s>>>(
-        static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k), int(q), tpw);
+    hipLaunchKernelGGL((circ_dctp_kernel<P, Io>), dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(S::K.nt),
+                       static_cast<size_t>(S::lds_bytes()), s, static_cast<const typename Io::T*>(x),
+                       static_cast<const typename Io::T*>(dy), dc, batch, int(k), int(q), tpw);
     st = launch_status();
     if (st != RDFFT_OK || dc_time_domain(P, false)) return st;
     return launch_rdfft<P, F32Io, true>(dc, q * k, s);  // dc holds packed spectra
@@ -215,10 +216,10 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
     const int64_t lds = lds_dx > lds_dc ? lds_dx : lds_dc;
     int st = launch_fill_zero(dc, q * k * P, s);
     if (st == RDFFT_OK) {
-      circ_bwd_kernel<P, Io><<<dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt), static_cast<size_t>(lds), s>>>(
-          static_cast<const typename Io::T*>(x), c, static_cast<const typename Io::T*>(dy),
-          static_cast<typename Io::T*>(dx), dc, batch, int(k), int(q), tpw_dc, int(gdx), int(gdy), ndc, tpw_dx,
-          int(gxx));
+      hipLaunchKernelGGL((circ_bwd_kernel<P, Io>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
+                         static_cast<size_t>(lds), s, static_cast<const typename Io::T*>(x), c,
+                         static_cast<const typename Io::T*>(dy), static_cast<typename Io::T*>(dx), dc, batch, int(k),
+                         int(q), tpw_dc, int(gdx), int(gdy), ndc, tpw_dx, int(gxx));
       st = launch_status();
     }
     *status = st;
@@ -315,8 +316,9 @@ int launch_cols(void* data, int64_t n, int64_t w, hipStream_t s) {
   using S = ColShape<H>;
   const int64_t ntiles = (w + S::CL - 1) / S::CL;
   if (n * ntiles > 0x7fffffff) return RDFFT_ERR_SIZE;
-  col_kernel<H, INV, Io><<<dim3(static_cast<unsigned>(n * ntiles)), dim3(S::NT), static_cast<size_t>(S::lds_bytes()), s>>>(
-      static_cast<typename Io::T*>(data), static_cast<int>(w), static_cast<int>(ntiles));
+  hipLaunchKernelGGL((col_kernel<H, INV, Io>), dim3(static_cast<unsigned>(n * ntiles)), dim3(S::NT),
+                     static_cast<size_t>(S::lds_bytes()), s, static_cast<typename Io::T*>(data), static_cast<int>(w),
+                     static_cast<int>(ntiles));
   return launch_status();
 }
 
@@ -343,8 +345,8 @@ template <class Io, bool INV>
 int launch_combine(void* data, int64_t n, int64_t h, int64_t w, hipStream_t s) {
   if (h < 4 || w < 4) return RDFFT_OK;  // no pair (j, k) with 0 < j < h/2 and 0 < k < w/2
   const int64_t total = n * (h / 2) * (w / 2);
-  combine_kernel<INV, Io><<<dim3(elementwise_grid(total)), dim3(256), 0, s>>>(
-      static_cast<typename Io::T*>(data), n, ilog2(static_cast<int>(h)), ilog2(static_cast<int>(w)));
+  hipLaunchKernelGGL((combine_kernel<INV, Io>), dim3(elementwise_grid(total)), dim3(256), 0, s,
+                     static_cast<typename Io::T*>(data), n, ilog2(static_cast<int>(h)), ilog2(static_cast<int>(w)));
   return launch_status();
 }
 
@@ -378,9 +380,9 @@ int spectrum_entry(const void* packed, const float* spec, int64_t rows, int64_t 
     using Io = decltype(io);
     auto* z = static_cast<typename Io::T*>(const_cast<void*>(packed));
     if (PACK)
-      pack_kernel<Io><<<dim3(grid), dim3(256), 0, s>>>(spec, z, rows, lp);
+      hipLaunchKernelGGL((pack_kernel<Io>), dim3(grid), dim3(256), 0, s, spec, z, rows, lp);
     else
-      unpack_kernel<Io><<<dim3(grid), dim3(256), 0, s>>>(z, const_cast<float*>(spec), rows, lp);
+      hipLaunchKernelGGL((unpack_kernel<Io>), dim3(grid), dim3(256), 0, s, z, const_cast<float*>(spec), rows, lp);
     return launch_status();
   });
 }

@@ -102,8 +102,8 @@ int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t
 
 /*
  * circulant_bwd -- gradients of the layer above for an upstream gradient dy
- * (the pages: products of packed spectra stay conjugate-symmetric, gradients
- * likewise):
+ * (Paper-Notes page, section "循环矩阵训练适配": the gradients are again
+ * products of packed spectra, which stay conjugate-symmetric):
  *     dx[b, j-block] = IFFT( sum_i conj(FFT(c[i, j])) * FFT(dy[b, i-block]) )   (= dy W)
  *     dc[i, j, :]    = IFFT( sum_b conj(FFT(x[b, j-block])) * FFT(dy[b, i-block]) )
  *   x   [batch, d_in]   dtype, read only

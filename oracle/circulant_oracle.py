@@ -30,7 +30,8 @@ Two independent formulations:
         y_i  = IFFT( sum_j FFT(c_ij) * FFT(x_j) )
         dx_j = IFFT( sum_i conj(FFT(c_ij)) * FFT(dy_i) )
         dc_ij = IFFT( sum_b conj(FFT(x_bj)) * FFT(dy_bi) )
-    (the pages: "gradients likewise keep the symmetry").
+    (Paper-Notes page, section "循环矩阵训练适配": the gradients are products
+    of packed spectra as well, so they stay conjugate-symmetric).
 """
 
 from __future__ import annotations

@@ -132,8 +132,10 @@ def test_backward_single_outputs(batch, d, p, dtype):
         assert row_relerr(to_f64(dx), dxo) <= TOL[dtype]
     for dc in (dc_both, dc_only):
         assert row_relerr(to_f64(dc).reshape(-1, p), dco.reshape(-1, p)) <= TOL["f32"]
-    # the dx products are the same arithmetic in either launch
-    assert torch.equal(dx_both, dx_only)
+    # the same products in either launch, up to the compiler's fusing of
+    # multiplies into adds, which may differ between two kernels: rounding-level
+    # agreement (one storage rounding for 16-bit outputs)
+    assert row_relerr(to_f64(dx_both), to_f64(dx_only)) <= {"f32": 1e-6, "bf16": 4e-3, "f16": 5e-4}[dtype]
 
 
 def test_empty_batch():
@@ -161,3 +163,31 @@ def test_identity_and_shift_weights():
     torch.cuda.synchronize()
     assert np.allclose(to_f64(y), xr, atol=1e-5)
     assert np.allclose(to_f64(y2), np.roll(xr[:, :p], 3, axis=1), atol=1e-5)
+
+
+@pytest.mark.parametrize("batch,d,p,dtype", [(256, 4096, 128, "bf16"), (256, 4096, 4096, "bf16"), (64, 1024, 1024, "f32"),
+                                             (33, 256, 16, "f32")])
+def test_repeatability(batch, d, p, dtype):
+    """Ten calls on the same inputs: y and dx are bitwise identical (each
+    output element is computed by one thread in a fixed order); dc sums its
+    token ranges with atomic adds in no fixed order, so its repeats may differ
+    in the last bits, and only by rounding: every repeat stays within 1e-6
+    (normwise, per (i, j) row) of the first."""
+    q = k = d // p
+    x, _ = device_input((batch, d), syn.WL_TEST, syn.T_X, 31, dtype=dtype)
+    c, _ = device_input((q, k, p), syn.WL_TEST, syn.T_C, 31, scale=d**-0.5)
+    dy, _ = device_input((batch, d), syn.WL_TEST, syn.T_DY, 31, dtype=dtype)
+    _say(f"repeatability B={batch} D={d} p={p} {dtype}")
+    runs = []
+    for _ in range(10):
+        y = bcl.circulant_fwd(x, c)
+        dx, dc = bcl.circulant_bwd(x, c, dy)
+        runs.append((y, dx, dc))
+    torch.cuda.synchronize()
+    y0, dx0, dc0 = runs[0]
+    differ = 0
+    for y, dx, dc in runs[1:]:
+        assert torch.equal(y, y0) and torch.equal(dx, dx0)
+        differ += int(not torch.equal(dc, dc0))
+        assert row_relerr(to_f64(dc).reshape(-1, p), to_f64(dc0).reshape(-1, p)) <= 1e-6
+    _say(f"  dc differed from the first call in {differ} of 9 repeats")

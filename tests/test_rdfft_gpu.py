@@ -106,10 +106,15 @@ def test_inverse_accepts_any_packed_vector(p):
 def test_bitwise_deterministic(p, dtype):
     x, _ = device_input((1024, p), syn.WL_TEST, syn.T_X, 7, dtype=dtype)
     outs = []
-    for _ in range(5):
+    for _ in range(10):
         y = x.clone()
         bcl.rdfft_forward(y)
         outs.append(y)
+    torch.cuda.synchronize()
+    for y in outs[1:]:
+        assert torch.equal(y, outs[0])
+    for y in outs:
+        bcl.rdfft_inverse(y)
     torch.cuda.synchronize()
     for y in outs[1:]:
         assert torch.equal(y, outs[0])

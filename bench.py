@@ -48,6 +48,8 @@ METRIC = "rdFFT GB/s + % HBM peak (p=512,4096); circulant fwd+bwd tokens/s"
 HBM_PEAK_GBS = 8000.0
 VALU_FP32_PEAK_TFS = 157.3
 ROTATE_BYTES = 1 << 30
+# timed regions of at most this many launches are queued as plain launches
+MAX_QUEUED_LAUNCHES = 1024
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "block_circulant_layers_amd", "csrc")
 
@@ -181,12 +183,14 @@ def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
     one batch: step g runs the forward on buffer g mod nbuf and the inverse on
     buffer (g + nbuf/2) mod nbuf, so a buffer's forward and its inverse are
     nbuf/2 steps (1 GiB of traffic) apart and neither reads from a cache.
-    Steps are launched in runs of up to nbuf/2 from HIP graphs (cached per run
-    position, all captured before the timed region): the run's forwards, then
-    its inverses, with events between them, giving the mean duration of a
-    forward and of an inverse launch in the timed region.  A bounded spin
-    kernel holds the GPU while the host queues the timed runs, so the events
-    time back-to-back GPU execution."""
+    Steps run in runs of up to nbuf/2: the run's forwards, then its
+    inverses, with events between them, giving the mean duration of a forward
+    and of an inverse launch in the timed region.  A bounded spin kernel holds
+    the GPU while the host queues the timed region, so the events time
+    back-to-back GPU execution.  Timed regions of up to MAX_QUEUED_LAUNCHES
+    launches are queued as plain launches; longer ones replay HIP graphs
+    (cached per run position, all captured before the timed region), which
+    cost about 10 us of GPU time per graph launch."""
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     eb = 4 if dtype == "f32" else 2
     nbytes = rows * p * eb
@@ -197,32 +201,38 @@ def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
     base = syn.torch_normal((rows, p), workload, syn.T_X, index, dtype=tdt)
     bufs = [base.clone() for _ in range(nbuf)]
     graphs = {}
+    # a short timed region is queued as plain launches behind the spin kernel
+    # (no per-graph launch cost); a long one replays cached graphs
+    queued = eager or 2 * steps <= MAX_QUEUED_LAUNCHES
 
-    def run_fns(g, n):
+    def run_fns(g, n, plain=False):
+        fwd = lambda g=g, n=n: [bcl.rdfft_forward(bufs[(g + i) % nbuf]) for i in range(n)]  # noqa: E731
+        inv = lambda g=g, n=n: [bcl.rdfft_inverse(bufs[(g + half + i) % nbuf]) for i in range(n)]  # noqa: E731
+        if plain:
+            return fwd, inv
         key = (g % nbuf, n)
         if key not in graphs:
-            fwd = lambda g=g, n=n: [bcl.rdfft_forward(bufs[(g + i) % nbuf]) for i in range(n)]  # noqa: E731
-            inv = lambda g=g, n=n: [bcl.rdfft_inverse(bufs[(g + half + i) % nbuf]) for i in range(n)]  # noqa: E731
-            graphs[key] = (_replayer(fwd, eager), _replayer(inv, eager))
+            graphs[key] = (_replayer(fwd, False), _replayer(inv, False))
         return graphs[key]
 
-    # capture every run's graphs before anything is timed
     warm_runs = step_runs(0, warmup, chunk)
     timed_runs = step_runs(warmup, steps, chunk)
-    for g, n in warm_runs + timed_runs:
-        run_fns(g, n)
+    if not queued:  # capture every run's graphs before anything is timed
+        for g, n in warm_runs + timed_runs:
+            run_fns(g, n)
     for g, n in warm_runs:
-        f, i = run_fns(g, n)
+        f, i = run_fns(g, n, plain=queued)
         f()
         i()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in timed_runs]
     tm = Timer()
     torch.cuda.synchronize()
-    hold_gpu(1.0 + 0.15 * len(timed_runs))  # the runs are queued before the GPU starts them
+    # hold the GPU while the host queues the timed region
+    hold_gpu(2.0 + (0.04 * 2 * steps if queued else 0.15 * len(timed_runs)))
     tm.start()
     for (g, n), e in zip(timed_runs, ev):
-        f, i = run_fns(g, n)
+        f, i = run_fns(g, n, plain=queued)
         e[0].record()
         f()
         e[1].record()
@@ -252,6 +262,7 @@ def bench_rdfft(rows, p, dtype, steps, warmup, workload, index=0, eager=False):
         "fwd_ms": fwd_ms,
         "inv_ms": inv_ms,
         "nbuf": nbuf,
+        "queued": queued,
         "roundtrip_drift": drift,
     }
 
@@ -665,6 +676,141 @@ def trace_summary(trace_dir: str, steps: int, warmup: int, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+CALIB_KIB = 262144.0  # the --calib-copy copy: 256 MiB read and 256 MiB written
+
+
+def _counter_means(csv_path: str):
+    """{kernel name: (mean counter value, dispatches)} of one rocprofv3 --pmc
+    run, and the counter value of its first plain device copy (the
+    --calib-copy copy of known size), in KiB."""
+    import csv
+
+    acc, calib = {}, None
+    for r in csv.DictReader(open(csv_path)):
+        name, v = r["Kernel_Name"], float(r["Counter_Value"])
+        if name == "__amd_rocclr_copyBuffer" and calib is None:
+            calib = v
+        a = acc.setdefault(name, [0.0, 0])
+        a[0] += v
+        a[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}, calib
+
+
+def counter_summary(root: str):
+    """Markdown summaries of the HBM counter runs under ``root`` (the layout of
+    the commands quoted in them): (profiles/traffic.md text, profiles/
+    traffic_circulant_d4096.md text).  FETCH_SIZE and WRITE_SIZE are scaled by
+    the factor that maps the known copy onto its size."""
+    import glob
+
+    io = {"f32": "F32Io", "bf16": "Bf16Io", "f16": "F16Io"}
+    rows_md = []
+    calib_md = []
+    for fdir in sorted(glob.glob(os.path.join(root, "pmc", "FETCH_SIZE_*"))):
+        tag = os.path.basename(fdir)[len("FETCH_SIZE_"):]
+        p, dt = tag.split("_")
+        f, fcal = _counter_means(os.path.join(fdir, "pmc_counter_collection.csv"))
+        w, wcal = _counter_means(os.path.join(root, "pmc", f"WRITE_SIZE_{tag}", "pmc_counter_collection.csv"))
+        ff, wf = CALIB_KIB / fcal, CALIB_KIB / wcal
+        calib_md.append(f"| 4096x{p} {dt} | {fcal:.1f} | {ff:.5f} | {wcal:.1f} | {wf:.5f} |")
+        eb = 4 if dt == "f32" else 2
+        algo = 2 * 4096 * int(p) * eb
+        for kind in ("fwd", "inv"):
+            key = next(k for k in f if f"rdfft_{kind}_kernel<{p}, rdfft::{io[dt]}>" in k)
+            fk, n = f[key]
+            wk, _ = w[key]
+            scaled = (fk * ff + wk * wf) * 1024
+            rows_md.append(f"| rdfft_{kind}_kernel<{p}, {io[dt]}> 4096x{p} | {n} | {fk:.1f} | {wk:.1f} | "
+                           f"{scaled:.0f} | {algo} | {scaled / algo:.4f} |")
+    tr = "\n".join([
+        "# HBM traffic of the transform kernels (rocprofv3 counters)",
+        "",
+        f"source_hash: {kernel_source_hash()}",
+        "(hash of rdfft_device.hpp, rdfft_kernels.hpp and gen_twiddles.py as measured; bench.py reports",
+        "`roofline.traffic` only while the current sources hash to this value)",
+        "",
+        "Commands (one counter per run, repository root, one MI355X; `<p> <dtype>` = `512 f32`, `4096 f32`, "
+        "`4096 bf16`):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/FETCH_SIZE_<p>_<dtype> -o pmc --output-format csv -- python3 -u "
+        "bench.py --rows 4096 --p <p> --dtype <dtype> --steps 128 --warmup 1 --no-extra --no-cpu --calib-copy --eager",
+        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/WRITE_SIZE_<p>_<dtype> -o pmc --output-format csv -- python3 -u "
+        "bench.py --rows 4096 --p <p> --dtype <dtype> --steps 128 --warmup 1 --no-extra --no-cpu --calib-copy --eager",
+        "python3 bench.py --counter-summary gpurun_out",
+        "```",
+        "",
+        "`--calib-copy` first runs one plain 256 MiB device copy (`__amd_rocclr_copyBuffer`, the first copy dispatch",
+        "of the run); `--eager` launches the transforms directly so that every dispatch is counted.  Values are KiB",
+        "per dispatch, mean over all dispatches of the kernel.",
+        "",
+        "Calibration with the known-size copy (256 MiB = 262144 KiB read and written):",
+        "",
+        "| run | FETCH_SIZE of the copy | factor | WRITE_SIZE of the copy | factor |",
+        "|---|---|---|---|---|",
+        *calib_md,
+        "",
+        "Per launch (scaled; algorithmic = each row read once and written once):",
+        "",
+        "| kernel workload | dispatches | FETCH raw KiB | WRITE raw KiB | scaled bytes per launch | algorithmic | ratio |",
+        "|---|---|---|---|---|---|---|",
+        *rows_md,
+    ]) + "\n"
+    # circulant kernels of --profile-circulant (D=4096 bf16 workloads)
+    ctr = os.path.join(root, "ctr")
+    circ = None
+    if os.path.isdir(os.path.join(ctr, "FETCH_SIZE")):
+        f, fcal = _counter_means(os.path.join(ctr, "FETCH_SIZE", "pmc_counter_collection.csv"))
+        w, wcal = _counter_means(os.path.join(ctr, "WRITE_SIZE", "pmc_counter_collection.csv"))
+        if fcal is None or wcal is None:
+            raise SystemExit("the circulant counter runs carry no calibration copy (take them with --calib-copy)")
+        ff, wf = CALIB_KIB / fcal, CALIB_KIB / wcal
+        kib = lambda b: b / 1024  # noqa: E731
+        work = [  # (kernel, workload, algorithmic reads KiB, algorithmic writes KiB)
+            ("circ_tp_kernel<1024, false, rdfft::Bf16Io>", "adapter forward", kib(2048 * 4096 * 2 + 16 * 1024 * 4),
+             kib(2048 * 4096 * 2)),
+            ("circ_bwd_kernel<1024, rdfft::Bf16Io>", "adapter backward (dx and dc)",
+             kib(2 * 2048 * 4096 * 2 + 16 * 1024 * 4), kib(2048 * 4096 * 2 + 16 * 1024 * 4)),
+        ]
+        for pp in (128, 512, 4096):
+            cb = 4096 * 4096 // pp * 4
+            work.append((f"circ_tp_kernel<{pp}, false, rdfft::Bf16Io>", f"D=4096 B=256 p={pp} forward",
+                         kib(256 * 4096 * 2 + cb), kib(256 * 4096 * 2)))
+            work.append((f"circ_bwd_kernel<{pp}, rdfft::Bf16Io>", f"p={pp} backward (dx and dc)",
+                         kib(2 * 256 * 4096 * 2 + cb), kib(256 * 4096 * 2 + cb)))
+        lines = []
+        for kname, wl, ar, aw in work:
+            key = next((k for k in f if kname in k), None)
+            if key is None:
+                continue
+            fr, n = f[key]
+            wr, _ = w[key]
+            lines.append(f"| `{kname.replace('rdfft::', '')}` | {wl} | {n} | {ar:.0f} | {fr * ff:.0f} | "
+                         f"{fr * ff / ar:.2f} | {aw:.0f} | {wr * wf:.0f} | {wr * wf / aw:.2f} |")
+        circ = "\n".join([
+            "# HBM traffic of the circulant kernels (rocprofv3 counters), D=4096 bf16 workloads",
+            "",
+            "Commands (repository root, one MI355X):",
+            "",
+            "```",
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/ctr/FETCH_SIZE -o pmc --output-format csv -- python3 -u bench.py "
+            "--profile-circulant --calib-copy",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/ctr/WRITE_SIZE -o pmc --output-format csv -- python3 -u bench.py "
+            "--profile-circulant --calib-copy",
+            "python3 bench.py --counter-summary gpurun_out",
+            "```",
+            "",
+            f"Means over the dispatches of each kernel, KiB, scaled by the known-size copy (FETCH x {ff:.4f}, "
+            f"WRITE x {wf:.4f}).  Algorithmic: activations once, `c` once, `dc` once (fp32).",
+            "",
+            "| kernel | workload | dispatches | algorithmic reads | measured reads | ratio | algorithmic writes | "
+            "measured writes | ratio |",
+            "|---|---|---|---|---|---|---|---|---|",
+            *lines,
+        ]) + "\n"
+    return tr, circ
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -682,10 +828,19 @@ def main():
                     help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
     ap.add_argument("--profile-circulant", action="store_true",
                     help="only launch the circulant workloads eagerly, for counter collection, and exit")
+    ap.add_argument("--counter-summary", metavar="ROOT",
+                    help="write profiles/traffic.md and profiles/traffic_circulant_d4096.md from the FETCH_SIZE / "
+                         "WRITE_SIZE runs under ROOT (see those files for the commands) and exit (no GPU needed)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write the markdown summary of a rocprofv3 kernel trace of this script (csv files under "
                          "DIR, taken with the same --steps/--warmup) to stdout and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.counter_summary:
+        tr, circ = counter_summary(args.counter_summary)
+        open(os.path.join(PROFILES, "traffic.md"), "w").write(tr)
+        if circ:
+            open(os.path.join(PROFILES, "traffic_circulant_d4096.md"), "w").write(circ)
+        return
     if args.trace_summary:
         cmd = (f"rocprofv3 --kernel-trace --stats -d {args.trace_summary} -o ktrace --output-format csv -- "
                f"python3 -u bench.py --steps {args.steps} --warmup {args.warmup}")
@@ -703,9 +858,6 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     bcl.lib()
-    if args.profile_circulant:
-        profile_circulant()
-        return
     if args.calib_copy:
         a = torch.ones(64 << 20, device="cuda:0")
         b = torch.empty_like(a)
@@ -713,6 +865,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.profile_circulant:
+        profile_circulant()
+        return
 
     rows, p, dt = args.rows, args.p, args.dtype
     log(f"headline: rdfft {rows}x{p} {dt} fwd+inv, warmup {args.warmup}, steps {args.steps}")
@@ -739,7 +894,8 @@ def main():
             "rows": rows,
             "p": p,
             "rotating_buffers": h["nbuf"],
-            "launch": "eager launches" if args.eager else "HIP graph replays, runs of up to rotating_buffers / 2 steps",
+            "launch": ("plain launches queued behind a spin kernel" if h["queued"] else
+                       "HIP graph replays, runs of up to rotating_buffers / 2 steps"),
             "roundtrip_drift": h["roundtrip_drift"],
             "pct_hbm_peak": round(100 * h["gbs"] / HBM_PEAK_GBS, 2),
         },

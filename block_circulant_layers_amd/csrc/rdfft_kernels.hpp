@@ -27,11 +27,14 @@ __host__ __device__ constexpr int wg_threads(int P, int E) {
 __host__ __device__ constexpr int standalone_elems(int P, bool /*f32*/) { return elems_per_thread(P); }
 // resident workgroups per CU the standalone kernels are launched for (fp32
 // rows of p >= 1024: two workgroups, each looping over more groups, measured
-// faster than four; a second group of look-ahead measured slower; 16-bit rows
-// of 1024 <= p <= 4096: four; p = 8192 (512 threads): two, as four would cap
-// registers at 64 and spill; p <= 512: eight one-wave workgroups)
-__host__ __device__ constexpr int wg_per_cu(int P, bool f32) {
-  return P >= 1024 ? (f32 || P >= 8192 ? 2 : 4) : 8;
+// faster than four; a second group of look-ahead measured slower; the fp32
+// forward at p = 2048 and 4096 takes three (4096x2048 16.5 -> 14.5 us,
+// 4096x4096 27.8 -> 26.5 us), while three slowed the inverse there and both
+// directions at p = 1024; 16-bit rows of 1024 <= p <= 4096: four; p = 8192
+// (512 threads): two, as four would cap registers at 64 and spill; p <= 512:
+// eight one-wave workgroups)
+__host__ __device__ constexpr int wg_per_cu(int P, bool f32, bool inv) {
+  return P >= 1024 ? (f32 || P >= 8192 ? ((!inv && f32 && (P == 2048 || P == 4096)) ? 3 : 2) : 4) : 8;
 }
 // Forward kernels that stage the transformed row in LDS and store it in the
 // aligned element order t + T*s, instead of storing the last pass's packed
@@ -454,7 +457,7 @@ __device__ __forceinline__ void rdfft_inv_body(typename Io::T* __restrict__ data
 
 template <int P, class Io>
 __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io>())),
-                                  wg_per_cu(P, is_f32_io<Io>()) *
+                                  wg_per_cu(P, is_f32_io<Io>(), false) *
                                       wg_threads(P, standalone_elems(P, is_f32_io<Io>())) / 256)
     rdfft_fwd_kernel(typename Io::T* __restrict__ data, int64_t rows) {
   rdfft_fwd_body<P, Io>(data, rows);
@@ -462,7 +465,7 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
 
 template <int P, class Io>
 __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io>())),
-                                  wg_per_cu(P, is_f32_io<Io>()) *
+                                  wg_per_cu(P, is_f32_io<Io>(), true) *
                                       wg_threads(P, standalone_elems(P, is_f32_io<Io>())) / 256)
     rdfft_inv_kernel(typename Io::T* __restrict__ data, int64_t rows) {
   rdfft_inv_body<P, Io>(data, rows);

@@ -33,7 +33,7 @@ int launch_rdfft(void* data, int64_t rows, hipStream_t stream) {
   constexpr int NT = wg_threads(P, E);
   constexpr int ROWS = NT / (P / E);
   const int64_t groups = (rows + ROWS - 1) / ROWS;
-  const int64_t resident = static_cast<int64_t>(device_cus()) * wg_per_cu(P, is_f32_io<Io>());
+  const int64_t resident = static_cast<int64_t>(device_cus()) * wg_per_cu(P, is_f32_io<Io>(), INV);
   const int64_t grid = groups < resident ? groups : resident;
   auto* d = static_cast<typename Io::T*>(data);
   if (INV)

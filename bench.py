@@ -811,6 +811,82 @@ def counter_summary(root: str):
     return tr, circ
 
 
+def _sq_means(csv_path: str):
+    """{(kernel name, counter): mean value over its dispatches} of a rocprofv3 --pmc run."""
+    import csv
+
+    acc = {}
+    for r in csv.DictReader(open(csv_path)):
+        a = acc.setdefault((r["Kernel_Name"], r["Counter_Name"]), [0.0, 0])
+        a[0] += float(r["Counter_Value"])
+        a[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def sq_summary(root: str, trace_dir: str) -> str:
+    """Markdown summary of the SQ counter runs under ``root`` (cpmc/s1, cpmc/s2:
+    the circulant workloads; rpmc/s<i>_<dtype>: the 4096x4096 transforms),
+    with the traced durations of the same kernels from ``trace_dir``."""
+    import csv
+    import glob
+
+    m = {}
+    for path in glob.glob(os.path.join(root, "cpmc", "s*", "pmc_counter_collection.csv")) + \
+            glob.glob(os.path.join(root, "rpmc", "s*", "pmc_counter_collection.csv")):
+        m.update(_sq_means(path))
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    traced = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in csv.DictReader(open(stats[0]))} if stats else {}
+    clock, simds = 2.4e9, 1024
+    rows = []
+    kernels = sorted({k for k, _ in m if "rdfft::circ_" in k or "rdfft::rdfft_" in k})
+    for k in kernels:
+        g = lambda c: m.get((k, c))  # noqa: E731
+        if g("SQ_INSTS_VALU") is None or g("SQ_WAVE_CYCLES") is None:
+            continue
+        issue_us = g("SQ_INSTS_VALU") * 4 / (simds * clock) * 1e6
+        dur = next((v for n, v in traced.items() if n.split("(")[0] == k.split("(")[0]), None)
+        wait = g("SQ_WAIT_INST_ANY") / g("SQ_WAVE_CYCLES") if g("SQ_WAIT_INST_ANY") is not None else None
+        bank = (g("SQ_LDS_BANK_CONFLICT") / g("SQ_ACTIVE_INST_LDS")
+                if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_ACTIVE_INST_LDS") else None)
+        name = re.sub(r"rdfft::|^void ", "", k.split("(")[0])
+        rows.append(f"| `{name}` | {g('SQ_WAVES'):.0f} | {g('SQ_INSTS_VALU') / 1e6:.2f} | {g('SQ_INSTS_LDS') / 1e6:.2f} | "
+                    f"{issue_us:.1f} | {dur if dur is None else round(dur, 1)} | "
+                    f"{'-' if dur is None else round(issue_us / dur, 2)} | "
+                    f"{'-' if wait is None else round(wait, 2)} | {'-' if bank is None else round(bank, 2)} |")
+    return "\n".join([
+        "# SQ counters of the circulant kernels and the 4096x4096 transforms (rocprofv3)",
+        "",
+        "Commands (repository root, one MI355X; `<set>` is one of the two counter sets below, `<i>` its number):",
+        "",
+        "```",
+        "rocprofv3 --pmc <set> -d gpurun_out/cpmc/s<i> -o pmc --output-format csv -- python3 -u bench.py "
+        "--profile-circulant",
+        "rocprofv3 --pmc <set> -d gpurun_out/rpmc/s<i>_<dtype> -o pmc --output-format csv -- python3 -u bench.py "
+        "--rows 4096 --p 4096 --dtype <dtype> --steps 64 --warmup 1 --no-extra --no-cpu --eager",
+        "python3 bench.py --sq-summary gpurun_out",
+        "```",
+        "",
+        "Set 1: `SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_LDS "
+        "SQ_WAIT_INST_LDS SQ_WAIT_ANY`;",
+        "set 2: `SQ_INSTS_SALU SQ_ACTIVE_INST_LDS SQ_INST_CYCLES_VMEM SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT "
+        "SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE`.",
+        "`--profile-circulant` launches each circulant workload three times eagerly (forward, then backward with",
+        "dx and dc): one adapter of the 128-adapter workload (4096x4096, p=1024, 2048 tokens) and the single",
+        "layer D=4096, B=256 at p = 128, 512, 4096, all bf16.  Means over the dispatches of each kernel.",
+        "",
+        "*VALU issue time* = VALU wave-instructions x 4 cycles / (1024 SIMDs x 2.4 GHz): the time the",
+        "chip's SIMDs need just to issue them (one unpacked fp32 wave64 instruction occupies a SIMD for 4",
+        "cycles; packed fp32 is disabled in this build).  *Traced duration* is the kernel's average in",
+        "`kernel_trace_bench_default.md`.  *issue / duration* is the share of the kernel's time the VALUs are",
+        "busy at best.  The last column is SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.",
+        "",
+        "| kernel | waves | VALU wave-instr (M) | LDS instr (M) | VALU issue time (us) | traced duration (us) | "
+        "issue / duration | wait-for-issue / wave-cycles | bank-conflict cycles per LDS cycle |",
+        "|---|---|---|---|---|---|---|---|---|",
+        *rows,
+    ]) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -831,6 +907,9 @@ def main():
     ap.add_argument("--counter-summary", metavar="ROOT",
                     help="write profiles/traffic.md and profiles/traffic_circulant_d4096.md from the FETCH_SIZE / "
                          "WRITE_SIZE runs under ROOT (see those files for the commands) and exit (no GPU needed)")
+    ap.add_argument("--sq-summary", metavar="ROOT",
+                    help="write profiles/counters_circulant_and_transforms.md from the SQ counter runs under ROOT "
+                         "(and the kernel trace under ROOT/ktrace) and exit (no GPU needed)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write the markdown summary of a rocprofv3 kernel trace of this script (csv files under "
                          "DIR, taken with the same --steps/--warmup) to stdout and exit (no GPU needed)")
@@ -840,6 +919,10 @@ def main():
         open(os.path.join(PROFILES, "traffic.md"), "w").write(tr)
         if circ:
             open(os.path.join(PROFILES, "traffic_circulant_d4096.md"), "w").write(circ)
+        return
+    if args.sq_summary:
+        open(os.path.join(PROFILES, "counters_circulant_and_transforms.md"), "w").write(
+            sq_summary(args.sq_summary, os.path.join(args.sq_summary, "ktrace")))
         return
     if args.trace_summary:
         cmd = (f"rocprofv3 --kernel-trace --stats -d {args.trace_summary} -o ktrace --output-format csv -- "
@@ -908,8 +991,8 @@ def main():
             "traffic": recorded_traffic(f"{kname} {rows}x{p}"),
             "kernel": kname,
             "kernel_ms": round(h["fwd_ms"], 6),
-            "duration": "mean per forward launch in the timed region (HIP events around each run's graph of "
-                        "back-to-back forward launches, on the launch stream)",
+            "duration": "mean per forward launch in the timed region (HIP events, on the launch stream, around "
+                        "each run of back-to-back forward launches)",
             "kernel_ms_traced": traced,
             "frac_traced": None if traced is None else round(h["bytes_per_launch"] / (traced * 1e-3) / 1e9
                                                               / HBM_PEAK_GBS, 4),

@@ -11,7 +11,9 @@ from .binding import (  # noqa: F401
     RDFFT_F32,
     RdfftError,
     circulant_bwd,
+    circulant_bwd_acc,
     circulant_fwd,
+    circulant_fwd_zero,
     lib,
     lib_path,
     rdfft2d_forward,

@@ -23,6 +23,8 @@ __all__ = [
     "rdfft_inverse",
     "circulant_fwd",
     "circulant_bwd",
+    "circulant_fwd_zero",
+    "circulant_bwd_acc",
     "RDFFT_F32",
     "RDFFT_BF16",
     "RDFFT_F16",
@@ -49,6 +51,8 @@ SIGNATURES = {
     "rdfft_inverse": (ctypes.c_int, [_VP, _I64, _I64, ctypes.c_int, _VP]),
     "circulant_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "circulant_bwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_fwd_zero": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_bwd_acc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_unpack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_pack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft2d_forward": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
@@ -183,6 +187,43 @@ def circulant_bwd(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: torch.
     _call("circulant_bwd", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
           dx.data_ptr() if dx is not None else None, dc.data_ptr() if dc is not None else None,
           batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
+    return dx, dc
+
+
+def circulant_fwd_zero(x: torch.Tensor, c: torch.Tensor, dc: torch.Tensor, y: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """:func:`circulant_fwd` that also sets ``dc`` (float32, the shape of c) to
+    zero in the same launch, ready for :func:`circulant_bwd_acc`; returns y."""
+    q, k, p, batch = _circ_dims(x, c)
+    if y is None:
+        y = torch.empty(*x.shape[:-1], q * p, dtype=x.dtype, device=x.device)
+    _check_gpu(x, c, y, dc)
+    if y.dtype != x.dtype:
+        raise ValueError("y must have the dtype of x")
+    if dc.dtype != torch.float32 or dc.shape != c.shape:
+        raise ValueError("dc must be float32 with the shape of c")
+    _call("circulant_fwd_zero", x.device, x.data_ptr(), c.data_ptr(), y.data_ptr(), dc.data_ptr(), batch, k * p,
+          q * p, p, _dtype_code(x), _stream(x, stream))
+    return y
+
+
+def circulant_bwd_acc(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dc: torch.Tensor,
+                      dx: torch.Tensor | None = None, need_dx: bool = True, stream=None):
+    """Like :func:`circulant_bwd`, but the weight gradient is ADDED into ``dc``
+    (float32, the shape of c); returns (dx, dc)."""
+    q, k, p, batch = _circ_dims(x, c)
+    if need_dx and dx is None:
+        dx = torch.empty_like(x)
+    _check_gpu(x, c, dy, dx, dc)
+    if dy.dtype != x.dtype or (dx is not None and dx.dtype != x.dtype):
+        raise ValueError("dy and dx must have the dtype of x")
+    if dy.numel() != batch * q * p:
+        raise ValueError("dy must have shape (..., d_out)")
+    if dc.dtype != torch.float32 or dc.shape != c.shape:
+        raise ValueError("dc must be float32 with the shape of c")
+    _call("circulant_bwd_acc", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
+          dx.data_ptr() if dx is not None else None, dc.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
+          _stream(x, stream))
     return dx, dc
 
 

@@ -105,7 +105,8 @@ int launch_fill_zero(float* p, int64_t n, hipStream_t s) {
 }
 
 template <int P, class Io>
-int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s) {
+int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s,
+                   bool acc) {
   constexpr DcParams K = dc_params(P);
   const int64_t gy = (q + K.ti - 1) / K.ti, gz = (k + K.tj - 1) / K.tj;
   if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
@@ -115,7 +116,10 @@ int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int6
   tpw = (tpw + K.tb - 1) / K.tb * K.tb;
   const int64_t gx = (batch + tpw - 1) / tpw;
   if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
-  int st = launch_fill_zero(dc, q * k * P, s);
+  // the kernel adds packed spectra into dc, which the inverse at the end
+  // transforms back: start from zero, or (accumulating) from the spectra of
+  // what dc holds, so that the inverse returns old dc + the new sum
+  int st = acc ? launch_rdfft<P, F32Io, false>(dc, q * k, s) : launch_fill_zero(dc, q * k * P, s);
   if (st != RDFFT_OK) return st;
   hipLaunchKernelGGL((circ_dc_kernel<P, Io>), dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(K.nt), 0, s,
                      static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k),
@@ -170,7 +174,7 @@ int launch_circ_product(const void* in, const float* c, void* out, int64_t batch
 
 template <int P, class Io>
 int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s,
-                       bool zeroed) {
+                       bool zeroed, bool acc) {
   if constexpr (P >= 64) {
     using S = DtpShape<P>;
     const int64_t gy = (q + S::K.ti - 1) / S::K.ti, gz = (k + S::K.tj - 1) / S::K.tj;
@@ -178,7 +182,14 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
     const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb, S::K.wgs);
     const int64_t gx = (batch + tpw - 1) / tpw;
     if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
-    int st = zeroed ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);
+    // accumulating into time-domain dc needs nothing first; into packed
+    // spectra, dc is transformed forward (see launch_circ_dc)
+    int st = RDFFT_OK;
+    if (acc) {
+      if (!dc_time_domain(P, false)) st = launch_rdfft<P, F32Io, false>(dc, q * k, s);
+    } else if (!zeroed) {
+      st = launch_fill_zero(dc, q * k * P, s);
+    }
     if (st != RDFFT_OK) return st;
     hipLaunchKernelGGL((circ_dctp_kernel<P, Io>), dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(S::K.nt),
                        static_cast<size_t>(S::lds_bytes()), s, static_cast<const typename Io::T*>(x),
@@ -187,7 +198,8 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
     if (st != RDFFT_OK || dc_time_domain(P, false)) return st;
     return launch_rdfft<P, F32Io, true>(dc, q * k, s);  // dc holds packed spectra
   } else {
-    return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s);
+    (void)zeroed;
+    return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s, acc);
   }
 }
 
@@ -197,7 +209,7 @@ constexpr int64_t kBwdDxWgs = 256;  // dx workgroups the fused token split aims 
 
 template <int P, class Io>
 bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
-                           int64_t k, int64_t q, hipStream_t s, int* status) {
+                           int64_t k, int64_t q, bool acc, hipStream_t s, int* status) {
   if constexpr (bwd_fusable<P>()) {
     using S = TpShape<P, true>;
     using D = DtpShape<P>;
@@ -214,7 +226,7 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
     if (nwg > 0x7fffffff || gdx > 0x7fffffff || gdy > 0x7fffffff || gxx > 0x7fffffff) return false;
     const int64_t lds_dx = S::lds_bytes(static_cast<int>(q)), lds_dc = D::lds_bytes();
     const int64_t lds = lds_dx > lds_dc ? lds_dx : lds_dc;
-    int st = launch_fill_zero(dc, q * k * P, s);
+    int st = acc ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);  // dc is added into in the time domain
     if (st == RDFFT_OK) {
       hipLaunchKernelGGL((circ_bwd_kernel<P, Io>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
                          static_cast<size_t>(lds), s, static_cast<const typename Io::T*>(x), c,
@@ -225,29 +237,39 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
     *status = st;
     return true;
   } else {
-    (void)x, (void)c, (void)dy, (void)dx, (void)dc, (void)batch, (void)k, (void)q, (void)s, (void)status;
+    (void)x, (void)c, (void)dy, (void)dx, (void)dc, (void)batch, (void)k, (void)q, (void)acc, (void)s, (void)status;
     return false;
   }
 }
 
+// forward; a non-null zero[q k P] (a gradient accumulator of c) is cleared by
+// the token-persistent kernel as a side job, or by a fill where another runs
 template <int P, class Io>
-int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, hipStream_t s) {
-  return launch_circ_product<P, Io>(x, c, y, batch, d_in / P, d_out / P, false, s);
+int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, hipStream_t s,
+               float* zero) {
+  const int64_t k = d_in / P, q = d_out / P;
+  bool zeroed = false;
+  const int st = launch_circ_product<P, Io>(x, c, y, batch, k, q, false, s, zero, zero ? q * k * P : 0, &zeroed);
+  if (st != RDFFT_OK || !zero || zeroed) return st;
+  return launch_fill_zero(zero, q * k * P, s);
 }
 
+// backward; acc: add the token sum into dc instead of overwriting it
 template <int P, class Io>
 int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
-               int64_t d_out, hipStream_t s) {
+               int64_t d_out, bool acc, hipStream_t s) {
   const int64_t k = d_in / P, q = d_out / P;
-  if (batch == 0) return dc ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
+  if (batch == 0) return (dc && !acc) ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
   int fused_status = RDFFT_OK;
-  if (dx && dc && launch_circ_bwd_fused<P, Io>(x, c, dy, dx, dc, batch, k, q, s, &fused_status)) return fused_status;
+  if (dx && dc && launch_circ_bwd_fused<P, Io>(x, c, dy, dx, dc, batch, k, q, acc, s, &fused_status))
+    return fused_status;
   bool zeroed = false;  // dc cleared by the dx kernel
   if (dx) {
-    const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s, dc, dc ? q * k * P : 0, &zeroed);
+    float* zero = acc ? nullptr : dc;
+    const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s, zero, zero ? q * k * P : 0, &zeroed);
     if (st != RDFFT_OK) return st;
   }
-  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s, zeroed);
+  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s, zeroed, acc);
   return RDFFT_OK;
 }
 
@@ -270,16 +292,16 @@ int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* d
 
 template <class Io>
 int circ_fwd_dispatch(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, int64_t p,
-                      hipStream_t s) {
-#define CALL(P) circ_fwd_p<P, Io>(x, c, y, batch, d_in, d_out, s)
+                      hipStream_t s, float* zero) {
+#define CALL(P) circ_fwd_p<P, Io>(x, c, y, batch, d_in, d_out, s, zero)
   RDFFT_P_SWITCH(p, CALL)
 #undef CALL
 }
 
 template <class Io>
 int circ_bwd_dispatch(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
-                      int64_t d_out, int64_t p, hipStream_t s) {
-#define CALL(P) circ_bwd_p<P, Io>(x, c, dy, dx, dc, batch, d_in, d_out, s)
+                      int64_t d_out, int64_t p, bool acc, hipStream_t s) {
+#define CALL(P) circ_bwd_p<P, Io>(x, c, dy, dx, dc, batch, d_in, d_out, acc, s)
   RDFFT_P_SWITCH(p, CALL)
 #undef CALL
 }
@@ -424,7 +446,18 @@ int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t
   if (st != RDFFT_OK || batch == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return rdfft::by_dtype(dtype, [&](auto io) {
-    return rdfft::circ_fwd_dispatch<decltype(io)>(x, c, y, batch, d_in, d_out, p, s);
+    return rdfft::circ_fwd_dispatch<decltype(io)>(x, c, y, batch, d_in, d_out, p, s, nullptr);
+  });
+}
+
+int circulant_fwd_zero(const void* x, const float* c, void* y, float* dc, int64_t batch, int64_t d_in, int64_t d_out,
+                       int64_t p, int dtype, void* stream) {
+  const int st = rdfft::check_circulant_fwd_zero(x, c, y, dc, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0) return rdfft::launch_fill_zero(dc, (d_out / p) * d_in, s);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_fwd_dispatch<decltype(io)>(x, c, y, batch, d_in, d_out, p, s, dc);
   });
 }
 
@@ -434,7 +467,17 @@ int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float
   if (st != RDFFT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return rdfft::by_dtype(dtype, [&](auto io) {
-    return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, s);
+    return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, false, s);
+  });
+}
+
+int circulant_bwd_acc(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
+                      int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream) {
+  const int st = rdfft::check_circulant_bwd(x, c, dy, dx, dc, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, true, s);
   });
 }
 

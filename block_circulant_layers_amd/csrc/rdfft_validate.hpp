@@ -82,6 +82,21 @@ inline int check_circulant_fwd(const void* x, const float* c, const void* y, int
   return RDFFT_OK;
 }
 
+// forward that also clears dc[q, k, p]: dc is required, even for an empty batch
+inline int check_circulant_fwd_zero(const void* x, const float* c, const void* y, const float* dc, int64_t batch,
+                                    int64_t d_in, int64_t d_out, int64_t p, int dtype) {
+  const int st = check_circulant_fwd(x, c, y, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  if (dc == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(dc)) return RDFFT_ERR_ALIGN;
+  if (batch == 0) return RDFFT_OK;
+  const int64_t eb = dtype_bytes(dtype);
+  const int64_t cb = (d_out / p) * d_in * 4;
+  if (overlaps(dc, cb, x, batch * d_in * eb) || overlaps(dc, cb, c, cb) || overlaps(dc, cb, y, batch * d_out * eb))
+    return RDFFT_ERR_ALIAS;
+  return RDFFT_OK;
+}
+
 inline int check_circulant_bwd(const void* x, const float* c, const void* dy, const void* dx, const float* dc,
                                int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype) {
   if (!valid_dtype(dtype)) return RDFFT_ERR_DTYPE;

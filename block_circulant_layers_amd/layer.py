@@ -5,10 +5,14 @@ parameters c of shape (q, k, p), y_i = sum_j IFFT(FFT(c_ij) * FFT(x_j)): block
 (i, j) is the circulant matrix whose first column is c_ij, applied to input
 chunk j and summed into output chunk i (Paper-Notes, "循环矩阵训练适配": the
 circulant product through the in-place transform and its use in training).
-Forward and backward run in the library's fused kernels (``circulant_fwd`` and
-``circulant_bwd``); nothing here computes, and there is no CPU path.  The
-backward recomputes FFT(x) from the saved input rather than saving spectra,
-so a layer keeps only what a dense Linear would keep (x and its parameters).
+Forward and backward run in the library's fused kernels; nothing here
+computes, and there is no CPU path.  When c needs a gradient, the forward
+(``circulant_fwd_zero``) also clears a buffer for it in the same launch and the
+backward (``circulant_bwd_acc``) adds the token sum into that buffer, so a
+step takes two launches and no separate clearing pass.  The backward
+recomputes FFT(x) from the saved input rather than saving spectra, so a layer
+keeps only what a dense Linear would keep (x, its parameters and, between the
+passes, the parameter-sized gradient buffer).
 """
 
 from __future__ import annotations
@@ -17,19 +21,28 @@ import math
 
 import torch
 
-from .binding import circulant_bwd, circulant_fwd
+from .binding import circulant_bwd, circulant_bwd_acc, circulant_fwd, circulant_fwd_zero
 
 __all__ = ["BlockCirculantFunction", "BlockCirculantLinear"]
 
 
 class BlockCirculantFunction(torch.autograd.Function):
-    """y = block-circulant(c) x per token; gradients dx and dc from one backward call."""
+    """y = block-circulant(c) x per token; gradients dx and dc from one backward call.
+
+    ``grad_buffer``: the caller will need dc (grad mode on and c requires it),
+    so the forward clears a gradient buffer in its launch.  Grad mode is off
+    inside ``forward``, hence the caller decides.
+    """
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, c: torch.Tensor) -> torch.Tensor:
+    def forward(ctx, x: torch.Tensor, c: torch.Tensor, grad_buffer: bool = False) -> torch.Tensor:
         x = x.contiguous()
         c = c.contiguous()
         ctx.save_for_backward(x, c)
+        ctx.dc = None
+        if grad_buffer and ctx.needs_input_grad[1]:
+            ctx.dc = torch.empty_like(c)  # cleared by the forward launch, filled by the backward
+            return circulant_fwd_zero(x, c, ctx.dc)
         return circulant_fwd(x, c)
 
     @staticmethod
@@ -37,9 +50,13 @@ class BlockCirculantFunction(torch.autograd.Function):
         x, c = ctx.saved_tensors
         need_dx, need_dc = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if not (need_dx or need_dc):
-            return None, None
+            return None, None, None
+        dc, ctx.dc = ctx.dc, None  # zeroed buffer: good for one backward only
+        if need_dc and dc is not None:
+            dx, dc = circulant_bwd_acc(x, c, dy.contiguous(), dc, need_dx=need_dx)
+            return dx, dc, None
         dx, dc = circulant_bwd(x, c, dy.contiguous(), need_dx=need_dx, need_dc=need_dc)
-        return dx, dc
+        return dx, dc, None
 
 
 class BlockCirculantLinear(torch.nn.Module):
@@ -61,7 +78,7 @@ class BlockCirculantLinear(torch.nn.Module):
         self.c = torch.nn.Parameter(c)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return BlockCirculantFunction.apply(x, self.c)
+        return BlockCirculantFunction.apply(x, self.c, torch.is_grad_enabled() and self.c.requires_grad)
 
     def extra_repr(self) -> str:
         return f"d_in={self.d_in}, d_out={self.d_out}, p={self.p}"

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RDFFT_ABI_VERSION 2
+#define RDFFT_ABI_VERSION 3
 
 /* storage types */
 #define RDFFT_F32 0
@@ -123,6 +123,33 @@ int circulant_fwd(const void* x, const float* c, void* y, int64_t batch, int64_t
  */
 int circulant_bwd(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
                   int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_fwd_zero -- circulant_fwd that also sets dc[q, k, p] (float) to
+ * zero, as a side job of the same launch where the forward runs its token-
+ * persistent kernel (otherwise with one more small launch).  dc is meant to be
+ * the gradient accumulator of c that circulant_bwd_acc adds into, so that a
+ * training step of the layer (Paper-Notes page, "循环矩阵训练适配") needs no
+ * separate clearing launch.  Arguments as circulant_fwd, plus
+ *   dc  [q, k, p]  float, written with zeros; required even when batch == 0;
+ *                  must not overlap x, c or y.
+ */
+int circulant_fwd_zero(const void* x, const float* c, void* y, float* dc, int64_t batch, int64_t d_in, int64_t d_out,
+                       int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_bwd_acc -- circulant_bwd that ADDS the token sum into dc instead
+ * of overwriting it (dc += sum over tokens; dx is still overwritten).  The
+ * arguments, their checks and the order-of-summation caveat are those of
+ * circulant_bwd.  dc must hold finite values on entry.  Where the token sum
+ * is gathered as packed spectra (p < 64; p = 64 and 128 when dx is NULL or the
+ * one-launch backward does not fit), the old dc is transformed to packed
+ * spectra first and returns to the time domain with the new sum, which is
+ * exact up to the fp32 rounding of those two transforms.  When batch == 0
+ * nothing is done.
+ */
+int circulant_bwd_acc(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
+                      int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
 
 /*
  * rdfft_unpack -- packed spectra to explicit complex bins (the packed layout

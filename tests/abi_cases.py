@@ -77,6 +77,44 @@ def _circ_bwd():
     return [(f, a, e) for a, e in cases]
 
 
+def _circ_fwd_zero():
+    # the argument checks of circulant_fwd, plus dc (4 x 4 x 16 fp32 = 1024 B);
+    # an empty batch still clears dc, so it would launch: not listed
+    f = "circulant_fwd_zero"
+    cases = [
+        ((A, C_, B_, None, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, None, 0, 64, 64, 16, F32), NULL),
+        ((None, C_, B_, DC, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DC, 2, 64, 64, 12, F32), SIZE),
+        ((A, C_, B_, DC, 2, 64, 72, 16, F32), SHAPE),
+        ((A, C_, B_, DC, 2, 64, 64, 16, 4), DTYPE),
+        ((A, C_, B_, 0x500008, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, 0x500008, 0, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, 0x300000 + 512, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, 0x200000 - 512, 2, 64, 64, 16, BF16), ALIAS),
+        ((A, C_, B_, 0x100000 + 16, 2, 64, 64, 16, F32), ALIAS),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
+def _circ_bwd_acc():
+    # the checks of circulant_bwd; an empty batch adds nothing and launches nothing
+    f = "circulant_bwd_acc"
+    cases = [
+        ((A, C_, B_, None, None, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, 0, 64, 64, 16, F32), OK),
+        ((A, C_, B_, None, DC, 0, 64, 64, 16, BF16), OK),
+        ((A, None, B_, DX, DC, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, 2, 64, 64, 8192, F32), SIZE),
+        ((A, C_, B_, DX, DC, 2, 48, 64, 32, F32), SHAPE),
+        ((A, C_, B_, DX, DC, 2, 64, 64, 16, -2), DTYPE),
+        ((A, C_, B_, DX, 0x500004, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, DX, 0x300000 + 1008, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, 0x500000 - 64, DC, 2, 64, 64, 16, F32), ALIAS),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
 def _spectrum(fn):
     # argument order: (source, destination, ...): packed then spec for unpack, spec then packed for pack
     cases = [((A, B_, 0, 512, F32), OK), ((None, B_, 4, 512, F32), NULL), ((A, None, 4, 512, BF16), NULL)]
@@ -96,5 +134,6 @@ def _rdfft2d(fn):
     return [(fn, a, e) for a, e in cases]
 
 
-CASES = (_rdfft("rdfft_forward") + _rdfft("rdfft_inverse") + _circ_fwd() + _circ_bwd() + _spectrum("rdfft_unpack")
+CASES = (_rdfft("rdfft_forward") + _rdfft("rdfft_inverse") + _circ_fwd() + _circ_bwd() + _circ_fwd_zero()
+         + _circ_bwd_acc() + _spectrum("rdfft_unpack")
          + _spectrum("rdfft_pack") + _rdfft2d("rdfft2d_forward") + _rdfft2d("rdfft2d_inverse"))

@@ -8,6 +8,9 @@
 //   run_abi pack       <rows> <p> <dtype> <spec> <packed>
 //   run_abi circ_fwd   <batch> <d_in> <d_out> <p> <dtype> <x> <c> <y>
 //   run_abi circ_bwd   <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <dx|-> <dc|->
+//   run_abi circ_step  <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <y> <dx|-> <dc>
+//                      (circulant_fwd_zero into a dc that holds garbage, then
+//                      circulant_bwd_acc twice: dc = 2 x the gradient)
 //   run_abi cases      (stdin: one call per line, "<entry point> <arg> ...", a
 //                      pointer argument as an integer address or "null"; prints
 //                      each call's status, one per line)
@@ -101,6 +104,12 @@ int call_case(const std::string& line) {
   if (f == "circulant_fwd" && n == 8)
     return circulant_fwd(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), num(4), num(5), num(6), num(7),
                          int(num(8)), nullptr);
+  if (f == "circulant_fwd_zero" && n == 9)
+    return circulant_fwd_zero(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), static_cast<float*>(ptr(4)), num(5),
+                              num(6), num(7), num(8), int(num(9)), nullptr);
+  if (f == "circulant_bwd_acc" && n == 10)
+    return circulant_bwd_acc(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
+                             num(6), num(7), num(8), num(9), int(num(10)), nullptr);
   if (f == "circulant_bwd" && n == 10)
     return circulant_bwd(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
                          num(6), num(7), num(8), num(9), int(num(10)), nullptr);
@@ -163,6 +172,25 @@ int main(int argc, char** argv) {
                        want_dc ? static_cast<float*>(dc.p) : nullptr, b, di, dout, p, dt, nullptr);
     if (want_dx) write_file(argv[10], dx);
     if (want_dc) write_file(argv[11], dc);
+  } else if (op == "circ_step" && argc == 13) {
+    const int64_t b = arg(argv, 2), di = arg(argv, 3), dout = arg(argv, 4), p = arg(argv, 5);
+    const int dt = static_cast<int>(arg(argv, 6));
+    Buf x = read_file(argv[7], b * di * esize(dt));
+    Buf c = read_file(argv[8], (dout / p) * di * 4);
+    Buf dy = read_file(argv[9], b * dout * esize(dt));
+    const bool want_dx = std::strcmp(argv[11], "-") != 0;
+    Buf y = alloc(b * dout * esize(dt));
+    Buf dx = alloc(b * di * esize(dt));
+    Buf dc = alloc((dout / p) * di * 4);
+    for (size_t i = 0; i < dc.n / 4; ++i) static_cast<float*>(dc.p)[i] = 12345.0f;  // cleared by the forward
+    st = circulant_fwd_zero(x.p, static_cast<const float*>(c.p), y.p, static_cast<float*>(dc.p), b, di, dout, p, dt,
+                            nullptr);
+    for (int rep = 0; rep < 2 && st == RDFFT_OK; ++rep)
+      st = circulant_bwd_acc(x.p, static_cast<const float*>(c.p), dy.p, want_dx ? dx.p : nullptr,
+                             static_cast<float*>(dc.p), b, di, dout, p, dt, nullptr);
+    write_file(argv[10], y);
+    if (want_dx) write_file(argv[11], dx);
+    write_file(argv[12], dc);
   } else if (op == "cases" && argc == 2) {
     char buf[4096];
     while (std::fgets(buf, sizeof(buf), stdin)) {

@@ -40,7 +40,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = _header_functions()
     assert set(names) == {"rdfft_abi_version", "rdfft_status_string", "rdfft_forward", "rdfft_inverse",
-                          "circulant_fwd", "circulant_bwd", "rdfft_unpack", "rdfft_pack",
+                          "circulant_fwd", "circulant_bwd", "circulant_fwd_zero", "circulant_bwd_acc",
+                          "rdfft_unpack", "rdfft_pack",
                           "rdfft2d_forward", "rdfft2d_inverse"}
     for n in names:
         assert hasattr(L, n), n
@@ -72,7 +73,8 @@ def test_case_constants_match_header():
 def test_validation(L, fn, args, want):
     f = getattr(L, fn)
     # pointer positions: every argument before the first size is a pointer
-    n_ptr = {"rdfft_forward": 1, "rdfft_inverse": 1, "circulant_fwd": 3, "circulant_bwd": 5, "rdfft_unpack": 2,
+    n_ptr = {"rdfft_forward": 1, "rdfft_inverse": 1, "circulant_fwd": 3, "circulant_bwd": 5,
+             "circulant_fwd_zero": 4, "circulant_bwd_acc": 5, "rdfft_unpack": 2,
              "rdfft_pack": 2, "rdfft2d_forward": 1, "rdfft2d_inverse": 1}[fn]
     cargs = [ctypes.c_void_p(a) if i < n_ptr and a is not None else (None if i < n_ptr else a)
              for i, a in enumerate(args)]

@@ -138,6 +138,41 @@ def test_backward_single_outputs(batch, d, p, dtype):
     assert row_relerr(to_f64(dx_both), to_f64(dx_only)) <= {"f32": 1e-6, "bf16": 4e-3, "f16": 5e-4}[dtype]
 
 
+@pytest.mark.parametrize("batch,d_in,d_out,p,dtype,want_dx", [
+    (33, 256, 128, 16, "f32", True), (256, 4096, 4096, 128, "bf16", True), (256, 4096, 4096, 128, "bf16", False),
+    (70, 1024, 2048, 64, "f16", False), (96, 2048, 2048, 512, "f32", True), (512, 4096, 4096, 1024, "bf16", True),
+    (256, 4096, 4096, 4096, "bf16", True), (64, 8192, 4096, 4096, "f32", False)])
+def test_zeroing_forward_and_accumulating_backward(batch, d_in, d_out, p, dtype, want_dx):
+    """circulant_fwd_zero gives circulant_fwd's y bit for bit and clears dc;
+    circulant_bwd_acc gives circulant_bwd's dx bit for bit and adds the
+    gradient into dc: after two calls dc = 2 x the oracle's gradient.  The
+    cases cover the forward's clearing side job and its separate fill (p = 16),
+    time-domain adds (the one-launch backward, dc alone from p = 256) and the
+    packed-spectra adds (dc alone at p = 64 and 128, every dc at p = 16)."""
+    q, k = d_out // p, d_in // p
+    x, xr = device_input((batch, d_in), syn.WL_TEST, syn.T_X, p + 5, dtype=dtype)
+    c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, p + 5, scale=d_in**-0.5, dtype="f32")
+    dy, dyr = device_input((batch, d_out), syn.WL_TEST, syn.T_DY, p + 5, dtype=dtype)
+    _say(f"circulant fwd_zero / bwd_acc B={batch} d_in={d_in} d_out={d_out} p={p} {dtype} dx={want_dx}")
+    dxo, dco = co.circulant_backward_fft(xr, cr, dyr)
+    dc = torch.full_like(c, 3.5)
+    y = bcl.circulant_fwd_zero(x, c, dc)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dc) == 0
+    assert torch.equal(y, bcl.circulant_fwd(x, c))
+    dx, _ = bcl.circulant_bwd_acc(x, c, dy, dc, need_dx=want_dx)
+    dx_ref, dc_ref = bcl.circulant_bwd(x, c, dy, need_dx=want_dx)
+    torch.cuda.synchronize()
+    if want_dx:
+        assert torch.equal(dx, dx_ref)
+        assert row_relerr(to_f64(dx), dxo) <= TOL[dtype]
+    assert row_relerr(to_f64(dc).reshape(-1, p), dco.reshape(-1, p)) <= TOL["f32"]
+    assert row_relerr(to_f64(dc).reshape(-1, p), to_f64(dc_ref).reshape(-1, p)) <= 1e-6
+    bcl.circulant_bwd_acc(x, c, dy, dc, need_dx=want_dx)
+    torch.cuda.synchronize()
+    assert row_relerr(to_f64(dc).reshape(-1, p), 2 * dco.reshape(-1, p)) <= TOL["f32"]
+
+
 def test_empty_batch():
     c = torch.randn(2, 2, 16, device="cuda:0")
     x = torch.empty(0, 32, device="cuda:0")
@@ -147,6 +182,16 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert y.shape == (0, 32)
     assert torch.count_nonzero(dc) == 0  # sum over no tokens
+    # the zeroing forward clears dc also for no tokens; the accumulating
+    # backward leaves it as it is
+    dc2 = torch.full_like(c, 5.0)
+    bcl.circulant_fwd_zero(x, c, dc2)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dc2) == 0
+    dc2.fill_(2.0)
+    bcl.circulant_bwd_acc(x, c, torch.empty(0, 32, device="cuda:0"), dc2)
+    torch.cuda.synchronize()
+    assert torch.all(dc2 == 2.0)
 
 
 def test_identity_and_shift_weights():

@@ -74,6 +74,26 @@ def test_grad_accumulates_and_partial_needs():
     assert torch.equal(x.grad, dx_ref)
 
 
+def test_second_backward_and_no_grad():
+    # the forward's cleared gradient buffer serves one backward; a second
+    # backward through the same graph (retain_graph) computes dc afresh, and
+    # autograd adds it into .grad.  Under no_grad the forward clears nothing.
+    x, xr = device_input((6, 512), syn.WL_TEST, syn.T_X, 14)
+    c, cr = device_input((4, 4, 128), syn.WL_TEST, syn.T_C, 14, scale=1 / 512**0.5)
+    dy, dyr = device_input((6, 512), syn.WL_TEST, syn.T_DY, 14)
+    layer = _layer_with(c)
+    y = layer(x)
+    y.backward(dy, retain_graph=True)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    _, dco = co.circulant_backward_fft(xr, cr, dyr)
+    assert row_relerr(to_f64(layer.c.grad).reshape(-1, 128), 2 * dco.reshape(-1, 128)) <= TOL["f32"]
+    with torch.no_grad():
+        y2 = layer(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y.detach())
+
+
 def test_token_axes_and_transposed_input():
     # activations shaped (sequences, tokens, features), the leading axes being
     # tokens alike, and a non-contiguous input (the layer makes it contiguous)

@@ -370,15 +370,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const typename Io::T
 
 // ---------------------------------------------------------------------------
 // exchange layouts: padding of layout B and item order of the pass reading
-// layout B, for rows of P with E = 16 per thread (B = 32: E = 32).  Chosen by
-// simulating the 32-bank conflicts of every LDS access of the pass schedule.
+// layout B, for rows of P with E = 16 per thread (E = 32 at P = 32768, whose
+// layouts are 32, 512 and 8192).  Chosen by simulating the bank conflicts of
+// every LDS access of the pass schedule: a wave's access is split into two
+// halves of 32 lanes, and each half takes as many cycles as the largest number
+// of distinct addresses that fall in one of 32 banks.  That count matches the
+// SQ_LDS_BANK_CONFLICT counter of the long-row kernels exactly: 1024 extra
+// cycles per row at 16384 (left as is: the conflict-free item order of its
+// pass 1024 measured slower, 1024x16384 fp32 forward 39.1 -> 39.8 us) and 37888
+// at 32768 with the layouts replaced here, which serialised the 64 lanes of
+// every write into layout 512 (512x32768 fp32 forward 73.0 -> 50.6 us).
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int lds_pad(int P, int B) {
-  return B <= 16 || B == 32 ? 1 : B == 128 ? (P <= 512 ? 8 : P == 1024 ? 4 : P == 2048 ? 2 : 1) : 0;
+  return B <= 16 || B == 32   ? 1
+         : B == 128           ? (P <= 512 ? 8 : P == 1024 ? 4 : P == 2048 ? 2 : 1)
+         : P == 32768 && B == 512 ? 1
+                                  : 0;
 }
 // true: items of the pass with input size B are numbered class-fastest
 // (k = item % (B/2)); false: residue-fastest (r' = item % NRES)
-__host__ __device__ constexpr bool class_fast(int P, int B) { return B == 128 && P >= 2048; }
+__host__ __device__ constexpr bool class_fast(int P, int B) {
+  return (B == 128 && P >= 2048) || (P == 32768 && B == 512);
+}
 
 // ---------------------------------------------------------------------------
 // one row of P reals, T = P/E threads (t = thread index within the row).

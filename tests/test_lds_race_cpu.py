@@ -84,9 +84,11 @@ def test_checker_reports_a_missing_barrier(exe):
 
 
 # rows per length: a few row groups per persistent workgroup and a ragged last group
+# (rows of 16384 and 32768: one workgroup per row)
 RDFFT_CASES = [(2, 1027, "f32"), (4, 1029, "f32"), (8, 1030, "f32"), (16, 1031, "f32"), (32, 517, "f32"),
                (64, 261, "f32"), (128, 133, "f32"), (256, 69, "f32"), (512, 35, "f32"), (1024, 19, "f32"),
                (2048, 11, "f32"), (4096, 5, "f32"), (8192, 5, "f32"), (16384, 2, "f32"), (32768, 2, "f32"),
+               (16384, 5, "bf16"), (32768, 3, "f16"),
                (128, 133, "bf16"), (256, 69, "f16"), (512, 35, "bf16"), (1024, 19, "bf16"), (4096, 9, "bf16"),
                (4096, 9, "f16"), (8192, 5, "bf16")]
 

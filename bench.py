@@ -631,6 +631,17 @@ def profile_circulant(reps=3):
         log(f"profiled circulant {name}: B={batch} D={d} p={p}, {reps} x (forward, backward)")
 
 
+def profile_2d(reps=3):
+    """Eager 2D forward and inverse of one 4096x4096 fp32 array, for counter
+    collection under a profiler: no graphs, no timing."""
+    x = syn.torch_normal((1, 4096, 4096), syn.WL_RDFFT_LARGE, syn.T_X, 2)
+    for _ in range(reps):
+        bcl.rdfft2d_forward(x)
+        bcl.rdfft2d_inverse(x)
+    torch.cuda.synchronize()
+    log(f"profiled 2D 4096x4096 fp32: {reps} x (forward, inverse)")
+
+
 def trace_summary(trace_dir: str, steps: int, warmup: int, command: str) -> str:
     """Markdown summary of a ``rocprofv3 --kernel-trace --stats`` run of this
     script (csv output in ``trace_dir``): every kernel of this library by total
@@ -644,7 +655,7 @@ def trace_summary(trace_dir: str, steps: int, warmup: int, command: str) -> str:
     trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not stats or not trace:
         raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {trace_dir}")
-    short = lambda n: re.sub(r"rdfft::|\(anonymous namespace\)::|^void ", "", n.split("(")[0])  # noqa: E731
+    short = lambda n: re.sub(r"rdfft::|^void ", "", n.replace("(anonymous namespace)::", "").split("(")[0])  # noqa: E731
     rows = [r for r in csv.DictReader(open(stats[0])) if "rdfft::" in r["Name"] or "stream_inplace" in r["Name"]]
     lines = [
         "# Kernel trace: bench.py",
@@ -842,7 +853,7 @@ def sq_summary(root: str, trace_dir: str) -> str:
     traced = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in csv.DictReader(open(stats[0]))} if stats else {}
     clock, simds = 2.4e9, 1024
     rows = []
-    kernels = sorted({k for k, _ in m if "rdfft::circ_" in k or "rdfft::rdfft_" in k})
+    kernels = sorted({k for k, _ in m if any(f"rdfft::{n}_" in k for n in ("circ", "rdfft", "col", "combine"))})
     for k in kernels:
         g = lambda c: m.get((k, c))  # noqa: E731
         if g("SQ_INSTS_VALU") is None or g("SQ_WAVE_CYCLES") is None:
@@ -856,9 +867,10 @@ def sq_summary(root: str, trace_dir: str) -> str:
         rows.append(f"| `{name}` | {g('SQ_WAVES'):.0f} | {g('SQ_INSTS_VALU') / 1e6:.2f} | {g('SQ_INSTS_LDS') / 1e6:.2f} | "
                     f"{issue_us:.1f} | {dur if dur is None else round(dur, 1)} | "
                     f"{'-' if dur is None else round(issue_us / dur, 2)} | "
-                    f"{'-' if wait is None else round(wait, 2)} | {'-' if bank is None else round(bank, 2)} |")
+                    f"{'-' if wait is None else round(wait, 2)} | {'-' if bank is None else round(bank, 2)} | "
+                    f"{'-' if g('SQ_LDS_BANK_CONFLICT') is None else round(g('SQ_LDS_BANK_CONFLICT') / 1e6, 3)} |")
     return "\n".join([
-        "# SQ counters of the circulant kernels and the 4096x4096 transforms (rocprofv3)",
+        "# SQ counters of the circulant kernels, the 4096x4096 transforms, long rows and 2D (rocprofv3)",
         "",
         "Commands (repository root, one MI355X; `<set>` is one of the two counter sets below, `<i>` its number):",
         "",
@@ -867,6 +879,10 @@ def sq_summary(root: str, trace_dir: str) -> str:
         "--profile-circulant",
         "rocprofv3 --pmc <set> -d gpurun_out/rpmc/s<i>_<dtype> -o pmc --output-format csv -- python3 -u bench.py "
         "--rows 4096 --p 4096 --dtype <dtype> --steps 64 --warmup 1 --no-extra --no-cpu --eager",
+        "rocprofv3 --pmc <set> -d gpurun_out/rpmc/s<i>_long -o pmc --output-format csv -- python3 -u bench.py "
+        "--rows 512 --p 32768 --steps 16 --warmup 1 --no-extra --no-cpu --eager",
+        "rocprofv3 --pmc <set> -d gpurun_out/rpmc/s<i>_2d -o pmc --output-format csv -- python3 -u bench.py "
+        "--profile-2d",
         "python3 bench.py --sq-summary gpurun_out",
         "```",
         "",
@@ -876,17 +892,20 @@ def sq_summary(root: str, trace_dir: str) -> str:
         "SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE`.",
         "`--profile-circulant` launches each circulant workload three times eagerly (forward, then backward with",
         "dx and dc): one adapter of the 128-adapter workload (4096x4096, p=1024, 2048 tokens) and the single",
-        "layer D=4096, B=256 at p = 128, 512, 4096, all bf16.  Means over the dispatches of each kernel.",
+        "layer D=4096, B=256 at p = 128, 512, 4096, all bf16.  `--profile-2d` runs the 2D forward and inverse of",
+        "one 4096x4096 fp32 array three times.  Means over the dispatches of each kernel.",
         "",
         "*VALU issue time* = VALU wave-instructions x 4 cycles / (1024 SIMDs x 2.4 GHz): the time the",
         "chip's SIMDs need just to issue them (one unpacked fp32 wave64 instruction occupies a SIMD for 4",
         "cycles; packed fp32 is disabled in this build).  *Traced duration* is the kernel's average in",
         "`kernel_trace_bench_default.md`.  *issue / duration* is the share of the kernel's time the VALUs are",
-        "busy at best.  The last column is SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.",
+        "busy at best.  The last two columns are SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS and",
+        "SQ_LDS_BANK_CONFLICT itself (cycles summed over the chip, per dispatch).",
         "",
         "| kernel | waves | VALU wave-instr (M) | LDS instr (M) | VALU issue time (us) | traced duration (us) | "
-        "issue / duration | wait-for-issue / wave-cycles | bank-conflict cycles per LDS cycle |",
-        "|---|---|---|---|---|---|---|---|---|",
+        "issue / duration | wait-for-issue / wave-cycles | bank-conflict cycles per LDS cycle | "
+        "bank-conflict cycles (M) |",
+        "|---|---|---|---|---|---|---|---|---|---|",
         *rows,
     ]) + "\n"
 
@@ -908,6 +927,9 @@ def main():
                     help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
     ap.add_argument("--profile-circulant", action="store_true",
                     help="only launch the circulant workloads eagerly, for counter collection, and exit")
+    ap.add_argument("--profile-2d", action="store_true",
+                    help="only run the 2D forward and inverse of one 4096x4096 fp32 array eagerly, three times, for "
+                         "counter collection, and exit")
     ap.add_argument("--counter-summary", metavar="ROOT",
                     help="write profiles/traffic.md and profiles/traffic_circulant_d4096.md from the FETCH_SIZE / "
                          "WRITE_SIZE runs under ROOT (see those files for the commands) and exit (no GPU needed)")
@@ -954,6 +976,9 @@ def main():
         del a, b
     if args.profile_circulant:
         profile_circulant()
+        return
+    if args.profile_2d:
+        profile_2d()
         return
 
     rows, p, dt = args.rows, args.p, args.dtype

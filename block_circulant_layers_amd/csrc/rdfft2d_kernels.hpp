@@ -22,18 +22,28 @@ namespace rdfft {
 // a time (T = H/E threads per column, CP * T <= 1024 threads), and stores the
 // tile back the same way.  CL is the widest power of two whose tile fits the
 // LDS budget (64-byte runs from H = 2048 down, 32-byte runs at H = 4096).
+// LDS stride of a tile column.  In the load and store loops a 32-lane half
+// wavefront covers 32/CL rows of the CL columns (CL < 32), or 32 columns of
+// one row: the column stride must be 32/CL modulo the 32 banks in the first
+// case, and odd in the second, for the half's addresses to fall in distinct
+// banks.  (An odd stride at CL = 8 and 16 gave 4- and 2-way conflicts: 3072
+// extra cycles per load or store loop of a 4096-row tile.)
+__host__ __device__ constexpr int col_stride(int lds, int cl) {
+  return cl >= 32 ? (lds | 1) : lds + ((32 / cl - lds % 32) + 32) % 32;
+}
+
 template <int H>
 struct ColShape {
   static constexpr int E = elems_per_thread(H);
   static constexpr int T = H / E;
-  static constexpr int CS = Row<H, E>::LDS | 1;  // odd stride: a slot of adjacent columns in different banks
-  static constexpr int CL0 = (144 * 1024) / (CS * 4);
+  static constexpr int CL0 = (144 * 1024) / ((Row<H, E>::LDS | 1) * 4);
   static constexpr int CL = CL0 >= 64 ? 64 : CL0 >= 32 ? 32 : CL0 >= 16 ? 16 : CL0 >= 8 ? 8 : 4;
+  static constexpr int CS = col_stride(Row<H, E>::LDS, CL);
   static constexpr int CP = cmin(CL, 1024 / T);
   static constexpr int NT = CP * T;
   static constexpr int NP = CL / CP;
   static constexpr int64_t lds_bytes() { return static_cast<int64_t>(CL) * CS * 4; }
-  static_assert(CL % CP == 0 && (H * CL) % NT == 0, "column tile");
+  static_assert(CL % CP == 0 && (H * CL) % NT == 0 && CL * CS * 4 <= 144 * 1024, "column tile");
 };
 
 // Workgroups are handed to the eight XCDs in turn (workgroup b to XCD b % 8),

@@ -21,14 +21,22 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _run(batch, d_in, d_out, p, dtype, workload=syn.WL_TEST, index=0, c_scale=1.0, dense=True):
+def _run(batch, d_in, d_out, p, dtype, workload=syn.WL_TEST, index=0, c_scale=1.0, dense=True, step=False):
+    """One forward and backward against the oracle.  step: the training-step
+    calls bench.py times (circulant_fwd_zero clearing a NaN-filled dc, then
+    circulant_bwd_acc adding into it) instead of circulant_fwd / circulant_bwd."""
     q, k = d_out // p, d_in // p
     x, xr = device_input((batch, d_in), workload, syn.T_X, index, dtype=dtype)
     c, cr = device_input((q, k, p), workload, syn.T_C, index, scale=c_scale, dtype="f32")
     dy, dyr = device_input((batch, d_out), workload, syn.T_DY, index, dtype=dtype)
-    _say(f"circulant fwd/bwd B={batch} d_in={d_in} d_out={d_out} p={p} dtype={dtype}")
-    y = bcl.circulant_fwd(x, c)
-    dx, dc = bcl.circulant_bwd(x, c, dy)
+    _say(f"circulant {'step' if step else 'fwd/bwd'} B={batch} d_in={d_in} d_out={d_out} p={p} dtype={dtype}")
+    if step:
+        dc = torch.full_like(c, float("nan"))
+        y = bcl.circulant_fwd_zero(x, c, dc)
+        dx, dc = bcl.circulant_bwd_acc(x, c, dy, dc)
+    else:
+        y = bcl.circulant_fwd(x, c)
+        dx, dc = bcl.circulant_bwd(x, c, dy)
     torch.cuda.synchronize()
     if dense:
         yo = co.circulant_forward_dense(xr, cr)
@@ -68,18 +76,20 @@ def test_parity_shapes(batch, d_in, d_out, p, dtype):
     _run(batch, d_in, d_out, p, dtype, index=p + d_in, dense=(d_in * d_out <= 4096 * 4096))
 
 
+@pytest.mark.parametrize("step", [False, True])
 @pytest.mark.parametrize("p", [128, 512, 4096])
-def test_workload_d4096_b256(p):
-    # single layer D = 4096, B = 256 tokens, bf16 activations, fp32 c ~ N(0, 1/D)
-    _run(256, 4096, 4096, p, "bf16", syn.WL_CIRC_LAYER, index=p, c_scale=1 / 64.0, dense=False)
+def test_workload_d4096_b256(p, step):
+    # single layer D = 4096, B = 256 tokens, bf16 activations, fp32 c ~ N(0, 1/D);
+    # both call forms (step: the form bench.py times)
+    _run(256, 4096, 4096, p, "bf16", syn.WL_CIRC_LAYER, index=p, c_scale=1 / 64.0, dense=False, step=step)
 
 
-@pytest.mark.parametrize("adapter", [0, 77])
-def test_workload_adapter_shape(adapter):
+@pytest.mark.parametrize("adapter,step", [(0, False), (77, False), (0, True), (127, True)])
+def test_workload_adapter_shape(adapter, step):
     # one of the 128 adapters of the 7B-decoder-shaped workload, at its full shape:
-    # 4096 x 4096, p = 1024 (4 x 4 blocks), 2048 tokens, bf16
-    (x, c, dy, y, dx, dc), _ = _run(2048, 4096, 4096, 1024, "bf16", syn.WL_CIRC_ADAPTERS, index=adapter,
-                                    c_scale=1 / 64.0, dense=False)
+    # 4096 x 4096, p = 1024 (4 x 4 blocks), 2048 tokens, bf16 (step: the form bench.py times)
+    _run(2048, 4096, 4096, 1024, "bf16", syn.WL_CIRC_ADAPTERS, index=adapter, c_scale=1 / 64.0, dense=False,
+         step=step)
 
 
 def test_adjoint_identities_on_gpu_outputs():

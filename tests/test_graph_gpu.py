@@ -66,6 +66,39 @@ def test_circulant_graph_replays(b, d, p):
         assert err <= 1e-5, (i, err)
 
 
+# the training-step calls: the forward clears dc in its launch (p = 128, 4096),
+# or with a fill kernel (p = 16); the backward adds into it, in the time domain
+# (one launch with dx) or as packed spectra after transforming dc (p = 64 without dx)
+@pytest.mark.parametrize("b,d,p,want_dx", [(64, 1024, 128, True), (32, 4096, 4096, True), (24, 256, 16, True),
+                                           (40, 512, 64, False)])
+def test_training_step_graph_replays(b, d, p, want_dx):
+    x, _ = device_input((b, d), syn.WL_TEST, syn.T_X, 34, dtype="bf16")
+    c, _ = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 34, scale=1 / 32)
+    dy, _ = device_input((b, d), syn.WL_TEST, syn.T_DY, 34, dtype="bf16")
+    y0 = bcl.circulant_fwd(x, c)
+    dx0, dc0 = bcl.circulant_bwd(x, c, dy, need_dx=want_dx)
+    y, dc = torch.empty_like(y0), torch.empty_like(dc0)
+    dx = torch.empty_like(x) if want_dx else None
+
+    def step():
+        bcl.circulant_fwd_zero(x, c, dc, y)
+        bcl.circulant_bwd_acc(x, c, dy, dc, dx=dx, need_dx=want_dx)
+
+    g = _capture(step)
+    for i in range(4):
+        for t in (y, dx, dc):
+            if t is not None:
+                t.fill_(float("nan"))  # eager work; the replay must clear or overwrite everything
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0), i
+        if want_dx:
+            assert torch.equal(dx, dx0), i
+        err = float((dc - dc0).norm() / dc0.norm())
+        assert err <= 1e-5, (i, err)
+
+
 def test_2d_and_spectrum_graph_replays():
     x0, _ = device_input((2, 256, 512), syn.WL_TEST, syn.T_X, 33)
     eager = x0.clone()

@@ -539,23 +539,34 @@ def circ_algorithmic(batch, d, p, eb):
     return nbytes, flops
 
 
-def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
+def circ_layer_setup(batch, d, p, nrot=32):
+    """The single-layer workload as bench_circ_layer times it: nrot token
+    batches (bf16), one c (fp32), and ``rot``, a rotation of nrot training
+    steps.  After a rotation ys[j] and dxs[j] hold step j's outputs and dc the
+    last step's gradient."""
     q = k = d // p
-    xs = [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, i, dtype=torch.bfloat16) for i in range(nrot)]
-    dys = [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, i, dtype=torch.bfloat16) for i in range(nrot)]
-    c = syn.torch_normal((q, k, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0)
-    ys = [torch.empty_like(x) for x in xs]
-    dxs = [torch.empty_like(x) for x in xs]
-    dc = torch.empty_like(c)
+    w = {"xs": [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, i, dtype=torch.bfloat16) for i in range(nrot)],
+         "dys": [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, i, dtype=torch.bfloat16)
+                 for i in range(nrot)],
+         "c": syn.torch_normal((q, k, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0)}
+    w["ys"] = [torch.empty_like(x) for x in w["xs"]]
+    w["dxs"] = [torch.empty_like(x) for x in w["xs"]]
+    w["dc"] = torch.empty_like(w["c"])
 
     def rot():
         # a training step of the layer: the forward clears dc in its launch,
         # the backward adds the token sum into it (two launches per step)
         for j in range(nrot):
-            bcl.circulant_fwd_zero(xs[j], c, dc, ys[j])
-            bcl.circulant_bwd_acc(xs[j], c, dys[j], dc, dx=dxs[j])
+            bcl.circulant_fwd_zero(w["xs"][j], w["c"], w["dc"], w["ys"][j])
+            bcl.circulant_bwd_acc(w["xs"][j], w["c"], w["dys"][j], w["dc"], dx=w["dxs"][j])
 
-    g = _graph(rot)
+    w["rot"] = rot
+    return w
+
+
+def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
+    w = circ_layer_setup(batch, d, p, nrot)  # kept alive: the graph holds raw pointers into it
+    g = _graph(w["rot"])
     for _ in range(max(1, -(-warmup // nrot))):
         g.replay()
     reps = max(1, -(-steps // nrot))
@@ -576,22 +587,33 @@ def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
     }
 
 
-def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=1024):
+def circ_adapters_setup(n_adapters=128, batch=2048, d=4096, p=1024):
+    """The adapter workload as bench_circ_adapters times it: per adapter a
+    token batch, an upstream gradient (bf16) and c (fp32), and ``step``: the
+    forwards of all adapters in order, then the backwards in reverse."""
     q = k = d // p
-    xs = [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_X, a, dtype=torch.bfloat16) for a in range(n_adapters)]
-    dys = [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_DY, a, dtype=torch.bfloat16) for a in range(n_adapters)]
-    cs = [syn.torch_normal((q, k, p), syn.WL_CIRC_ADAPTERS, syn.T_C, a, scale=1 / 64.0) for a in range(n_adapters)]
-    ys = [torch.empty_like(x) for x in xs]
-    dxs = [torch.empty_like(x) for x in xs]
-    dcs = [torch.empty_like(c) for c in cs]
+    w = {"xs": [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_X, a, dtype=torch.bfloat16)
+                for a in range(n_adapters)],
+         "dys": [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_DY, a, dtype=torch.bfloat16)
+                 for a in range(n_adapters)],
+         "cs": [syn.torch_normal((q, k, p), syn.WL_CIRC_ADAPTERS, syn.T_C, a, scale=1 / 64.0) for a in range(n_adapters)]}
+    w["ys"] = [torch.empty_like(x) for x in w["xs"]]
+    w["dxs"] = [torch.empty_like(x) for x in w["xs"]]
+    w["dcs"] = [torch.empty_like(c) for c in w["cs"]]
 
     def step():
         for a in range(n_adapters):
-            bcl.circulant_fwd_zero(xs[a], cs[a], dcs[a], ys[a])
+            bcl.circulant_fwd_zero(w["xs"][a], w["cs"][a], w["dcs"][a], w["ys"][a])
         for a in reversed(range(n_adapters)):
-            bcl.circulant_bwd_acc(xs[a], cs[a], dys[a], dcs[a], dx=dxs[a])
+            bcl.circulant_bwd_acc(w["xs"][a], w["cs"][a], w["dys"][a], w["dcs"][a], dx=w["dxs"][a])
 
-    g = _graph(step)
+    w["step"] = step
+    return w
+
+
+def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=1024):
+    w = circ_adapters_setup(n_adapters, batch, d, p)  # kept alive: the graph holds raw pointers into it
+    g = _graph(w["step"])
     for _ in range(warmup):
         g.replay()
     tm = Timer()

@@ -3,7 +3,12 @@
 The torch.fft forms that bench.py times beside the layer as context must be
 the same linear map as the block-circulant layer (Paper-Notes, "循环矩阵训练
 适配"): checked here against the oracle's dense forward and backward in float64.
+Also: the algorithmic byte and flop counts of the layer workloads, the split of
+the timed steps into runs (exactly the requested count), and the exit of a
+multi-GPU request.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -39,3 +44,27 @@ def test_circ_algorithmic_counts(p, nbytes, mflops):
     b, f = bench.circ_algorithmic(256, 4096, p, 2)
     assert b == nbytes
     assert f / 1e6 == pytest.approx(mflops, abs=0.05)
+
+
+@pytest.mark.parametrize("g0, n, chunk", [(0, 20, 64), (5, 20, 64), (60, 10, 64), (0, 2048, 64), (256, 2048, 64),
+                                          (3, 0, 64), (63, 1, 64), (7, 130, 8)])
+def test_step_runs_cover_exactly(g0, n, chunk):
+    # the timed steps are exactly the requested ones, split only at multiples
+    # of the rotation's half (a run's forwards and inverses never share a buffer)
+    runs = bench.step_runs(g0, n, chunk)
+    assert sum(m for _, m in runs) == n
+    g = g0
+    for start, m in runs:
+        assert start == g and m >= 1
+        assert start // chunk == (start + m - 1) // chunk
+        g += m
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr

@@ -483,6 +483,90 @@ __global__ void __launch_bounds__(wg_threads(P, standalone_elems(P, is_f32_io<Io
 __host__ __device__ constexpr int long_elems(int P) { return P >= 32768 ? 32 : 16; }
 constexpr int kMaxLongP = 32768;
 
+// One pass's twiddles, read from its table ahead of the pass: the long-row
+// kernels issue a pass's table reads before the barriers that precede it, so
+// their latency overlaps the previous pass's scatter instead of following it.
+template <int P, int E, int B, bool INV>
+struct AheadTws {
+  using Rw = Row<P, E>;
+  using PS = typename Rw::template Pass<B>;
+  using W = typename std::conditional<INV, Tw, TwF>::type;
+  W w[PS::IPT][PS::R];
+  // read through a buffer resource over the table: buffer loads are ordinary
+  // memory reads that the barriers' fences keep where they are issued (plain
+  // reads of the constant table may be sunk past a barrier to their first
+  // use), and they count only against the vector memory counter
+  __device__ __forceinline__ void load(int t) {
+    static_assert(PS::R % 2 == 0 && sizeof(W) == 8, "16-byte reads of two twiddles");
+    constexpr int NE = (B / 2) * PS::R;  // entries of the table: class k at [k R, k R + R)
+    const W* tab;
+    if constexpr (INV)
+      tab = PassTw<B, PS::R>::inv();
+    else
+      tab = PassTw<B, PS::R>::fwd();
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<W*>(tab), 0, NE * static_cast<int>(sizeof(W)), kBufWord3);
+#pragma unroll
+    for (int n = 0; n < PS::IPT; ++n) {
+      int rp, k;
+      PS::item(t + Rw::T * n, rp, k);  // k = 0 reads the table's first entries, unused
+#pragma unroll
+      for (int j = 0; j < PS::R; j += 2) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * PS::R + j) * static_cast<int>(sizeof(W)), 0, 0);
+        w[n][j] = W{__uint_as_float(v[0]), __uint_as_float(v[1])};
+        w[n][j + 1] = W{__uint_as_float(v[2]), __uint_as_float(v[3])};
+      }
+    }
+  }
+  template <int B2, class WW, int RR>
+  __device__ __forceinline__ void item(int n, int /*k*/, WW (&out)[RR]) const {
+    static_assert(B2 == B && RR == PS::R, "the twiddles of one pass");
+#pragma unroll
+    for (int j = 0; j < RR; ++j) out[j] = w[n][j];
+  }
+};
+
+// fwd_rest with each pass's twiddles issued ahead (tw: pass B's, already issued)
+template <int P, int E, int B, bool TO_LDS, class St, class TW>
+__device__ __forceinline__ void fwd_rest_ahead(float (&a)[E], float* L, int t, St st, const TW& tw) {
+  using Rw = Row<P, E>;
+  using PS = typename Rw::template Pass<B>;
+  __syncthreads();  // the previous pass's scatter is visible
+  Rw::template fwd_pass<B>(a, L, t, tw);
+  if constexpr (PS::BP == P && !TO_LDS) {
+    Rw::template last_store<B>(a, t, st);
+  } else if constexpr (PS::BP == P) {
+    __syncthreads();  // every gather of this exchange is done
+    Rw::template pass_scatter<B>(a, L, t);
+  } else {
+    AheadTws<P, E, PS::BP, false> next;
+    next.load(t);
+    __syncthreads();  // every gather of this exchange is done
+    Rw::template pass_scatter<B>(a, L, t);
+    fwd_rest_ahead<P, E, PS::BP, TO_LDS>(a, L, t, st, next);
+  }
+}
+
+// inv_down with each pass's twiddles issued ahead; on entry L holds the
+// spectra of size Bout (the caller has issued tw, pass pass_in_for(Bout)'s
+// twiddles, before its barrier)
+template <int P, int E, int Bout, class TW>
+__device__ __forceinline__ void inv_down_ahead(float (&a)[E], float* L, int t, const TW& tw) {
+  using Rw = Row<P, E>;
+  constexpr int B = Rw::pass_in_for(Bout);
+  Rw::template inv_pass<B>(a, [L](int v, int c) { return L[v + c]; }, t, tw);
+  __syncthreads();  // every gather of this exchange is done
+  Rw::template inv_scatter<B>(a, L, t);
+  if constexpr (B > E) {
+    AheadTws<P, E, Rw::pass_in_for(B), true> next;
+    next.load(t);
+    __syncthreads();
+    inv_down_ahead<P, E, B>(a, L, t, next);
+  } else {
+    __syncthreads();
+  }
+}
+
 template <int P, class Io>
 __global__ void __launch_bounds__(P / long_elems(P)) rdfft_fwd_long_kernel(typename Io::T* __restrict__ data) {
   constexpr int E = long_elems(P);
@@ -492,18 +576,19 @@ __global__ void __launch_bounds__(P / long_elems(P)) rdfft_fwd_long_kernel(typen
   RDFFT_DYNAMIC_LDS(lds);
   const int t = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + static_cast<int64_t>(blockIdx.x) * P, P);
-  const typename Rw::GlobalTws tw;
+  AheadTws<P, E, E, false> tw;
+  tw.load(t);
   float a[E];
   Rw::fwd_pass0(a, [rs](int v, int c) { return Io::widen(Io::template braw<row_load_aux(SEG)>(rs, v, c)); }, t);
   Rw::fwd_pass0_scatter(a, lds, t);
   auto st = [rs](int v, int c, float x) { Io::template bstore<row_store_aux(SEG)>(rs, v, c, x); };
   if constexpr (fwd_staged_store(P, is_f32_io<Io>())) {
-    fwd_rest<P, E, E, true>(a, lds, t, st, tw);
+    fwd_rest_ahead<P, E, E, true>(a, lds, t, st, tw);
     __syncthreads();  // the row is in lds[0..P) in natural packed order
 #pragma unroll
     for (int s = 0; s < E; ++s) Io::template bstore<row_store_aux_strided(SEG)>(rs, t, T * s, lds[t + T * s]);
   } else {
-    fwd_rest<P, E, E, false>(a, lds, t, st, tw);
+    fwd_rest_ahead<P, E, E, false>(a, lds, t, st, tw);
   }
 }
 
@@ -512,13 +597,20 @@ __global__ void __launch_bounds__(P / long_elems(P)) rdfft_inv_long_kernel(typen
   constexpr int E = long_elems(P);
   using Rw = Row<P, E>;
   constexpr int SEG = 64 * static_cast<int>(sizeof(typename Io::T));
+  constexpr int BL = Rw::pass_in_for(P);
   RDFFT_DYNAMIC_LDS(lds);
   const int t = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc<Io>(data + static_cast<int64_t>(blockIdx.x) * P, P);
-  const typename Rw::GlobalTws tw;
+  AheadTws<P, E, BL, true> tw;
+  tw.load(t);
   float a[E];
   auto ld = [rs](int v, int c) { return Io::widen(Io::template braw<row_load_aux(SEG)>(rs, v, c)); };
-  inv_rest<P, E, E, false>(a, lds, t, ld, tw);
+  Rw::template inv_pass<BL>(a, ld, t, tw);  // the first pass reads the packed row from HBM
+  AheadTws<P, E, Rw::pass_in_for(BL), true> next;
+  next.load(t);
+  Rw::template inv_scatter<BL>(a, lds, t);
+  __syncthreads();
+  inv_down_ahead<P, E, BL>(a, lds, t, next);
   auto st = [rs](int v, int c, float x) { Io::template bstore<row_store_aux_strided(SEG)>(rs, v, c, x); };
   Rw::inv_pass0_store(a, lds, t, 1.0f / static_cast<float>(P), st);
 }

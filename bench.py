@@ -919,7 +919,7 @@ def sq_summary(root: str, trace_dir: str) -> str:
         "",
         "*VALU issue time* = VALU wave-instructions x 4 cycles / (1024 SIMDs x 2.4 GHz): the time the",
         "chip's SIMDs need just to issue them (one unpacked fp32 wave64 instruction occupies a SIMD for 4",
-        "cycles; packed fp32 is disabled in this build).  *Traced duration* is the kernel's average in",
+        "cycles; the library is compiled with packed fp32 disabled).  *Traced duration* is the kernel's average in",
         "`kernel_trace_bench_default.md`.  *issue / duration* is the share of the kernel's time the VALUs are",
         "busy at best.  The last two columns are SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS and",
         "SQ_LDS_BANK_CONFLICT itself (cycles summed over the chip, per dispatch).",

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     RdfftError,
     circulant_bwd,
     circulant_bwd_acc,
+    circulant_bwd_det,
+    circulant_bwd_det_workspace,
     circulant_fwd,
     circulant_fwd_zero,
     lib,

@@ -25,6 +25,8 @@ __all__ = [
     "circulant_bwd",
     "circulant_fwd_zero",
     "circulant_bwd_acc",
+    "circulant_bwd_det",
+    "circulant_bwd_det_workspace",
     "RDFFT_F32",
     "RDFFT_BF16",
     "RDFFT_F16",
@@ -53,6 +55,9 @@ SIGNATURES = {
     "circulant_bwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "circulant_fwd_zero": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "circulant_bwd_acc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_bwd_det_workspace": (ctypes.c_int, [_I64, _I64, _I64, _I64, ctypes.c_int, ctypes.POINTER(_I64)]),
+    "circulant_bwd_det": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                         _VP]),
     "rdfft_unpack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_pack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft2d_forward": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
@@ -224,6 +229,42 @@ def circulant_bwd_acc(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dc: to
     _call("circulant_bwd_acc", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
           dx.data_ptr() if dx is not None else None, dc.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
           _stream(x, stream))
+    return dx, dc
+
+
+def circulant_bwd_det_workspace(batch: int, d_in: int, d_out: int, p: int, with_dx: bool = True) -> int:
+    """Bytes of the workspace :func:`circulant_bwd_det` needs for this shape."""
+    out = ctypes.c_int64(0)
+    st = lib().circulant_bwd_det_workspace(batch, d_in, d_out, p, int(bool(with_dx)), ctypes.byref(out))
+    if st != 0:
+        raise RdfftError("circulant_bwd_det_workspace", st)
+    return out.value
+
+
+def circulant_bwd_det(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor | None = None,
+                      dc: torch.Tensor | None = None, ws: torch.Tensor | None = None, need_dx: bool = True,
+                      stream=None):
+    """:func:`circulant_bwd` with a deterministic dc (bitwise the same from call
+    to call); ``ws`` is its workspace (float32, allocated here if None).
+    Returns (dx, dc); dc is overwritten."""
+    q, k, p, batch = _circ_dims(x, c)
+    if need_dx and dx is None:
+        dx = torch.empty_like(x)
+    if dc is None:
+        dc = torch.empty_like(c)
+    need = circulant_bwd_det_workspace(batch, k * p, q * p, p, dx is not None)
+    if ws is None:
+        ws = torch.empty(max(1, need // 4), dtype=torch.float32, device=x.device)
+    _check_gpu(x, c, dy, dx, dc, ws)
+    if dy.dtype != x.dtype or (dx is not None and dx.dtype != x.dtype):
+        raise ValueError("dy and dx must have the dtype of x")
+    if dy.numel() != batch * q * p:
+        raise ValueError("dy must have shape (..., d_out)")
+    if dc.dtype != torch.float32 or dc.shape != c.shape or ws.dtype != torch.float32:
+        raise ValueError("dc and ws must be float32, dc with the shape of c")
+    _call("circulant_bwd_det", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
+          dx.data_ptr() if dx is not None else None, dc.data_ptr(), ws.data_ptr(), ws.numel() * 4,
+          batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
     return dx, dc
 
 

@@ -104,26 +104,66 @@ int launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return launch_status();
 }
 
-template <int P, class Io>
-int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s,
-                   bool acc) {
+// grid of a weight-gradient launch: gx token ranges of tpw tokens times gy x gz
+// tiles of (i, j); ok = false when it exceeds the launch limits
+struct DcSplit {
+  int64_t gx, gy, gz, tpw;
+  bool ok;
+};
+
+template <int P>
+DcSplit dc_split_small(int64_t batch, int64_t k, int64_t q) {
   constexpr DcParams K = dc_params(P);
-  const int64_t gy = (q + K.ti - 1) / K.ti, gz = (k + K.tj - 1) / K.tj;
-  if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
-  int64_t want_x = kDcTargetWgs / (gy * gz);
+  DcSplit d{};
+  d.gy = (q + K.ti - 1) / K.ti;
+  d.gz = (k + K.tj - 1) / K.tj;
+  if (d.gy > 65535 || d.gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return d;
+  int64_t want_x = kDcTargetWgs / (d.gy * d.gz);
   if (want_x < 1) want_x = 1;
   int64_t tpw = (batch + want_x - 1) / want_x;
-  tpw = (tpw + K.tb - 1) / K.tb * K.tb;
-  const int64_t gx = (batch + tpw - 1) / tpw;
-  if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
+  d.tpw = (tpw + K.tb - 1) / K.tb * K.tb;
+  d.gx = (batch + d.tpw - 1) / d.tpw;
+  d.ok = d.gx <= 0x7fffffff;
+  return d;
+}
+
+// the fixed-order sum of a deterministic dc (parts slices of the workspace ws),
+// then the inverse where the slices hold packed spectra
+template <int P>
+int launch_dc_reduce(const float* ws, float* dc, int64_t n, int64_t parts, bool spectra, hipStream_t s) {
+  const int64_t blocks = (n + kReduceEl - 1) / kReduceEl;
+  if (parts > 0x7fffffff || blocks > 0x7fffffff) return RDFFT_ERR_SIZE;
+  hipLaunchKernelGGL((dc_reduce_kernel), dim3(static_cast<unsigned>(blocks)), dim3(kReduceEl * kReduceGroups), 0, s,
+                     ws, dc, n, static_cast<int>(parts));
+  const int st = launch_status();
+  if (st != RDFFT_OK || !spectra) return st;
+  return launch_rdfft<P, F32Io, true>(dc, n / P, s);
+}
+
+// ws: deterministic mode, the partial sums stored into ws (one q k P slice per
+// token range) and summed in order into dc; otherwise added into dc atomically
+template <int P, class Io>
+int launch_circ_dc(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s,
+                   bool acc, float* ws) {
+  constexpr DcParams K = dc_params(P);
+  const DcSplit d = dc_split_small<P>(batch, k, q);
+  if (!d.ok) return RDFFT_ERR_SIZE;
+  const dim3 grid(unsigned(d.gx), unsigned(d.gy), unsigned(d.gz));
+  const auto* px = static_cast<const typename Io::T*>(x);
+  const auto* pdy = static_cast<const typename Io::T*>(dy);
+  if (ws) {
+    hipLaunchKernelGGL((circ_dc_kernel<P, Io, true>), grid, dim3(K.nt), 0, s, px, pdy, ws, batch, int(k), int(q),
+                       d.tpw);
+    const int st = launch_status();
+    if (st != RDFFT_OK) return st;
+    return launch_dc_reduce<P>(ws, dc, q * k * P, d.gx, true, s);
+  }
   // the kernel adds packed spectra into dc, which the inverse at the end
   // transforms back: start from zero, or (accumulating) from the spectra of
   // what dc holds, so that the inverse returns old dc + the new sum
   int st = acc ? launch_rdfft<P, F32Io, false>(dc, q * k, s) : launch_fill_zero(dc, q * k * P, s);
   if (st != RDFFT_OK) return st;
-  hipLaunchKernelGGL((circ_dc_kernel<P, Io>), dim3(unsigned(gx), unsigned(gy), unsigned(gz)), dim3(K.nt), 0, s,
-                     static_cast<const typename Io::T*>(x), static_cast<const typename Io::T*>(dy), dc, batch, int(k),
-                     int(q), tpw);
+  hipLaunchKernelGGL((circ_dc_kernel<P, Io>), grid, dim3(K.nt), 0, s, px, pdy, dc, batch, int(k), int(q), d.tpw);
   st = launch_status();
   if (st != RDFFT_OK) return st;
   return launch_rdfft<P, F32Io, true>(dc, q * k, s);
@@ -172,16 +212,36 @@ int launch_circ_product(const void* in, const float* c, void* out, int64_t batch
   return launch_circ_mm<P, Io>(in, c, out, batch, nin, nout, trans, s);
 }
 
+// split of the token-persistent weight-gradient tiles, `target` workgroups aimed at
+template <int P>
+DcSplit dc_split_tp(int64_t batch, int64_t k, int64_t q, int64_t target) {
+  using S = DtpShape<P>;
+  DcSplit d{};
+  d.gy = (q + S::K.ti - 1) / S::K.ti;
+  d.gz = (k + S::K.tj - 1) / S::K.tj;
+  if (d.gy > 65535 || d.gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return d;
+  d.tpw = tokens_per_wg(batch, d.gy * d.gz, S::K.tb, target);
+  d.gx = (batch + d.tpw - 1) / d.tpw;
+  d.ok = d.gx <= 0x7fffffff;
+  return d;
+}
+
 template <int P, class Io>
 int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, int64_t k, int64_t q, hipStream_t s,
-                       bool zeroed, bool acc) {
+                       bool zeroed, bool acc, float* ws) {
   if constexpr (P >= 64) {
     using S = DtpShape<P>;
-    const int64_t gy = (q + S::K.ti - 1) / S::K.ti, gz = (k + S::K.tj - 1) / S::K.tj;
-    if (gy > 65535 || gz > 65535 || k > 0x7fffffff || q > 0x7fffffff) return RDFFT_ERR_SIZE;
-    const int64_t tpw = tokens_per_wg(batch, gy * gz, S::K.tb, S::K.wgs);
-    const int64_t gx = (batch + tpw - 1) / tpw;
-    if (gx > 0x7fffffff) return RDFFT_ERR_SIZE;
+    const DcSplit d = dc_split_tp<P>(batch, k, q, S::K.wgs);
+    if (!d.ok) return RDFFT_ERR_SIZE;
+    const int64_t gx = d.gx, gy = d.gy, gz = d.gz, tpw = d.tpw;
+    if (ws) {
+      hipLaunchKernelGGL((circ_dctp_kernel<P, Io, true>), dim3(unsigned(gx), unsigned(gy), unsigned(gz)),
+                         dim3(S::K.nt), static_cast<size_t>(S::lds_bytes()), s, static_cast<const typename Io::T*>(x),
+                         static_cast<const typename Io::T*>(dy), ws, batch, int(k), int(q), tpw);
+      const int st = launch_status();
+      if (st != RDFFT_OK) return st;
+      return launch_dc_reduce<P>(ws, dc, q * k * P, gx, !dc_time_domain(P, false), s);
+    }
     // accumulating into time-domain dc needs nothing first; into packed
     // spectra, dc is transformed forward (see launch_circ_dc)
     int st = RDFFT_OK;
@@ -199,7 +259,7 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
     return launch_rdfft<P, F32Io, true>(dc, q * k, s);  // dc holds packed spectra
   } else {
     (void)zeroed;
-    return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s, acc);
+    return launch_circ_dc<P, Io>(x, dy, dc, batch, k, q, s, acc, ws);
   }
 }
 
@@ -207,18 +267,29 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
 // the dx tiles fit; returns false when the caller must take the two-kernel path.
 constexpr int64_t kBwdDxWgs = 256;  // dx workgroups the fused token split aims at
 
+// whether dx and dc of this shape run in one launch (circ_bwd_kernel)
+template <int P>
+bool bwd_fused_shape(int64_t k, int64_t q) {
+  if constexpr (bwd_fusable<P>()) {
+    using S = TpShape<P, true>;
+    return q <= S::CR && S::fits(static_cast<int>(q)) && S::lds_bytes(static_cast<int>(q)) <= kMaxLds &&
+           k <= 0x7fffffff;
+  } else {
+    (void)k, (void)q;
+    return false;
+  }
+}
+
 template <int P, class Io>
 bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
-                           int64_t k, int64_t q, bool acc, hipStream_t s, int* status) {
+                           int64_t k, int64_t q, bool acc, float* ws, hipStream_t s, int* status) {
   if constexpr (bwd_fusable<P>()) {
     using S = TpShape<P, true>;
     using D = DtpShape<P>;
-    if (q > S::CR || !S::fits(static_cast<int>(q)) || S::lds_bytes(static_cast<int>(q)) > kMaxLds ||
-        k > 0x7fffffff)
-      return false;
-    const int64_t gdy = (q + D::K.ti - 1) / D::K.ti, gdz = (k + D::K.tj - 1) / D::K.tj;
-    const int64_t tpw_dc = tokens_per_wg(batch, gdy * gdz, D::K.tb, D::K.fwgs);
-    const int64_t gdx = (batch + tpw_dc - 1) / tpw_dc;
+    if (!bwd_fused_shape<P>(k, q)) return false;
+    const DcSplit d = dc_split_tp<P>(batch, k, q, D::K.fwgs);
+    if (!d.ok) return false;
+    const int64_t gdy = d.gy, gdz = d.gz, tpw_dc = d.tpw, gdx = d.gx;
     const int64_t gxy = (k + S::K.to - 1) / S::K.to;
     const int64_t tpw_dx = tokens_per_wg(batch, gxy, S::K.tb, kBwdDxWgs);
     const int64_t gxx = (batch + tpw_dx - 1) / tpw_dx;
@@ -226,18 +297,30 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
     if (nwg > 0x7fffffff || gdx > 0x7fffffff || gdy > 0x7fffffff || gxx > 0x7fffffff) return false;
     const int64_t lds_dx = S::lds_bytes(static_cast<int>(q)), lds_dc = D::lds_bytes();
     const int64_t lds = lds_dx > lds_dc ? lds_dx : lds_dc;
-    int st = acc ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);  // dc is added into in the time domain
-    if (st == RDFFT_OK) {
-      hipLaunchKernelGGL((circ_bwd_kernel<P, Io>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
-                         static_cast<size_t>(lds), s, static_cast<const typename Io::T*>(x), c,
-                         static_cast<const typename Io::T*>(dy), static_cast<typename Io::T*>(dx), dc, batch, int(k),
-                         int(q), tpw_dc, int(gdx), int(gdy), ndc, tpw_dx, int(gxx));
+    const auto* px = static_cast<const typename Io::T*>(x);
+    const auto* pdy = static_cast<const typename Io::T*>(dy);
+    auto* pdx = static_cast<typename Io::T*>(dx);
+    int st = RDFFT_OK;
+    if (ws) {
+      hipLaunchKernelGGL((circ_bwd_kernel<P, Io, true>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
+                         static_cast<size_t>(lds), s, px, c, pdy, pdx, ws, batch, int(k), int(q), tpw_dc, int(gdx),
+                         int(gdy), ndc, tpw_dx, int(gxx));
       st = launch_status();
+      if (st == RDFFT_OK) st = launch_dc_reduce<P>(ws, dc, q * k * P, gdx, false, s);  // time-domain slices
+    } else {
+      st = acc ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);  // dc is added into in the time domain
+      if (st == RDFFT_OK) {
+        hipLaunchKernelGGL((circ_bwd_kernel<P, Io>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
+                           static_cast<size_t>(lds), s, px, c, pdy, pdx, dc, batch, int(k), int(q), tpw_dc, int(gdx),
+                           int(gdy), ndc, tpw_dx, int(gxx));
+        st = launch_status();
+      }
     }
     *status = st;
     return true;
   } else {
-    (void)x, (void)c, (void)dy, (void)dx, (void)dc, (void)batch, (void)k, (void)q, (void)acc, (void)s, (void)status;
+    (void)x, (void)c, (void)dy, (void)dx, (void)dc, (void)batch, (void)k, (void)q, (void)acc, (void)ws, (void)s,
+        (void)status;
     return false;
   }
 }
@@ -254,22 +337,39 @@ int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_
   return launch_fill_zero(zero, q * k * P, s);
 }
 
-// backward; acc: add the token sum into dc instead of overwriting it
+// token ranges of the weight-gradient launch a backward of this shape takes
+// (with dx or without): the slices a deterministic dc needs in its workspace
+template <int P>
+int64_t dc_token_ranges(int64_t batch, int64_t k, int64_t q, bool with_dx) {
+  if (batch == 0) return 0;
+  DcSplit d{};
+  if constexpr (P >= 64) {
+    d = (with_dx && bwd_fused_shape<P>(k, q)) ? dc_split_tp<P>(batch, k, q, DtpShape<P>::K.fwgs)
+                                              : dc_split_tp<P>(batch, k, q, DtpShape<P>::K.wgs);
+  } else {
+    (void)with_dx;
+    d = dc_split_small<P>(batch, k, q);
+  }
+  return d.ok ? d.gx : -1;
+}
+
+// backward; acc: add the token sum into dc instead of overwriting it;
+// ws: deterministic dc (see launch_circ_dc), overwritten, never with acc
 template <int P, class Io>
 int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
-               int64_t d_out, bool acc, hipStream_t s) {
+               int64_t d_out, bool acc, hipStream_t s, float* ws = nullptr) {
   const int64_t k = d_in / P, q = d_out / P;
   if (batch == 0) return (dc && !acc) ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
   int fused_status = RDFFT_OK;
-  if (dx && dc && launch_circ_bwd_fused<P, Io>(x, c, dy, dx, dc, batch, k, q, acc, s, &fused_status))
+  if (dx && dc && launch_circ_bwd_fused<P, Io>(x, c, dy, dx, dc, batch, k, q, acc, ws, s, &fused_status))
     return fused_status;
   bool zeroed = false;  // dc cleared by the dx kernel
   if (dx) {
-    float* zero = acc ? nullptr : dc;
+    float* zero = (acc || ws) ? nullptr : dc;
     const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s, zero, zero ? q * k * P : 0, &zeroed);
     if (st != RDFFT_OK) return st;
   }
-  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s, zeroed, acc);
+  if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s, zeroed, acc, ws);
   return RDFFT_OK;
 }
 
@@ -300,10 +400,27 @@ int circ_fwd_dispatch(const void* x, const float* c, void* y, int64_t batch, int
 
 template <class Io>
 int circ_bwd_dispatch(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
-                      int64_t d_out, int64_t p, bool acc, hipStream_t s) {
-#define CALL(P) circ_bwd_p<P, Io>(x, c, dy, dx, dc, batch, d_in, d_out, acc, s)
+                      int64_t d_out, int64_t p, bool acc, hipStream_t s, float* ws = nullptr) {
+#define CALL(P) circ_bwd_p<P, Io>(x, c, dy, dx, dc, batch, d_in, d_out, acc, s, ws)
   RDFFT_P_SWITCH(p, CALL)
 #undef CALL
+}
+
+// token ranges of the weight gradient (dims validated before); -1 past the launch limits
+inline int64_t dc_token_ranges_dispatch(int64_t batch, int64_t d_in, int64_t d_out, int64_t p, bool with_dx) {
+#define CALL(P) dc_token_ranges<P>(batch, d_in / P, d_out / P, with_dx)
+  RDFFT_P_SWITCH(p, CALL)
+#undef CALL
+}
+
+// bytes of a deterministic dc's workspace: one q k p slice of floats per token range
+inline int circ_det_workspace(int64_t batch, int64_t d_in, int64_t d_out, int64_t p, bool with_dx, int64_t* bytes) {
+  const int64_t ranges = dc_token_ranges_dispatch(batch, d_in, d_out, p, with_dx);
+  if (ranges < 0) return RDFFT_ERR_SIZE;
+  const int64_t slice = (d_out / p) * d_in;  // q k p floats
+  if (ranges > 0 && slice > (int64_t{1} << 62) / 4 / ranges) return RDFFT_ERR_SIZE;
+  *bytes = ranges * slice * 4;
+  return RDFFT_OK;
 }
 
 // call f(Io{}) with the storage type of dtype (validated before)
@@ -478,6 +595,28 @@ int circulant_bwd_acc(const void* x, const float* c, const void* dy, void* dx, f
   hipStream_t s = static_cast<hipStream_t>(stream);
   return rdfft::by_dtype(dtype, [&](auto io) {
     return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, true, s);
+  });
+}
+
+int circulant_bwd_det_workspace(int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int with_dx, int64_t* bytes) {
+  if (bytes == nullptr) return RDFFT_ERR_NULL;
+  const int st = rdfft::check_circulant_dims(batch, d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  return rdfft::circ_det_workspace(batch, d_in, d_out, p, with_dx != 0, bytes);
+}
+
+int circulant_bwd_det(const void* x, const float* c, const void* dy, void* dx, float* dc, float* ws, int64_t ws_bytes,
+                      int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream) {
+  int st = rdfft::check_circulant_bwd(x, c, dy, dx, dc, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  int64_t need = 0;
+  st = rdfft::circ_det_workspace(batch, d_in, d_out, p, dx != nullptr, &need);
+  if (st != RDFFT_OK) return st;
+  st = rdfft::check_det_workspace(x, c, dy, dx, dc, ws, ws_bytes, need, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, false, s, ws);
   });
 }
 

@@ -120,4 +120,23 @@ inline int check_circulant_bwd(const void* x, const float* c, const void* dy, co
   return RDFFT_OK;
 }
 
+// the workspace of a deterministic dc (after check_circulant_bwd): dc is
+// required; ws must hold `need` bytes (nothing when need == 0), be aligned and
+// overlap no other argument
+inline int check_det_workspace(const void* x, const float* c, const void* dy, const void* dx, const float* dc,
+                               const float* ws, int64_t ws_bytes, int64_t need, int64_t batch, int64_t d_in,
+                               int64_t d_out, int64_t p, int dtype) {
+  if (dc == nullptr) return RDFFT_ERR_NULL;
+  if (ws_bytes < 0 || ws_bytes < need) return RDFFT_ERR_SIZE;
+  if (need == 0) return RDFFT_OK;
+  if (ws == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(ws)) return RDFFT_ERR_ALIGN;
+  const int64_t eb = dtype_bytes(dtype);
+  const int64_t xb = batch * d_in * eb, yb = batch * d_out * eb, cb = (d_out / p) * d_in * 4;
+  if (overlaps(ws, need, x, xb) || overlaps(ws, need, c, cb) || overlaps(ws, need, dy, yb) ||
+      overlaps(ws, need, dc, cb) || (dx && overlaps(ws, need, dx, xb)))
+    return RDFFT_ERR_ALIAS;
+  return RDFFT_OK;
+}
+
 }  // namespace rdfft

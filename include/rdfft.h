@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RDFFT_ABI_VERSION 3
+#define RDFFT_ABI_VERSION 4
 
 /* storage types */
 #define RDFFT_F32 0
@@ -150,6 +150,33 @@ int circulant_fwd_zero(const void* x, const float* c, void* y, float* dc, int64_
  */
 int circulant_bwd_acc(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
                       int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_bwd_det_workspace -- bytes of the workspace circulant_bwd_det
+ * needs for this shape, with dx computed too (with_dx != 0) or not: one slice
+ * of q k p floats per token range of the weight-gradient launch.  0 when
+ * batch == 0.  The count depends on the shape only (not on dtype or device).
+ *   bytes  out, the byte count; must not be NULL
+ * Statuses as circulant_bwd's size and shape checks.
+ */
+int circulant_bwd_det_workspace(int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int with_dx, int64_t* bytes);
+
+/*
+ * circulant_bwd_det -- circulant_bwd with a deterministic dc (same gradients,
+ * Paper-Notes page, "循环矩阵训练适配"): each token range's partial sums are
+ * stored into its own slice of the caller's workspace instead of added into dc
+ * atomically, and one more launch sums the slices in a fixed order into dc.
+ * dc is then bitwise the same from call to call for the same inputs, shape and
+ * device model.  Arguments as circulant_bwd, plus
+ *   ws        device workspace of ws_bytes bytes, 16-byte aligned, holding at
+ *             least circulant_bwd_det_workspace(..., with_dx = dx != NULL)
+ *             bytes (status RDFFT_ERR_SIZE otherwise); its contents on entry do
+ *             not matter and are overwritten; it must not overlap any other
+ *             argument.  May be NULL when that size is 0.
+ * dc is required (not NULL) and overwritten; dx may be NULL.
+ */
+int circulant_bwd_det(const void* x, const float* c, const void* dy, void* dx, float* dc, float* ws, int64_t ws_bytes,
+                      int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
 
 /*
  * rdfft_unpack -- packed spectra to explicit complex bins (the packed layout

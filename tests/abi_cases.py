@@ -115,6 +115,43 @@ def _circ_bwd_acc():
     return [(f, a, e) for a, e in cases]
 
 
+def _circ_bwd_det():
+    # circulant_bwd's checks, then dc required and the workspace: 2 tokens of
+    # 64 features at p = 16 need one slice of 4 x 4 x 16 floats (1 KiB) per
+    # token range; an empty batch needs none (and would launch: not listed)
+    f = "circulant_bwd_det"
+    WS = 0x600000
+    cases = [
+        ((A, C_, B_, DX, None, WS, 1 << 20, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, None, None, WS, 1 << 20, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, None, 1 << 20, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, WS, 0, 2, 64, 64, 16, F32), SIZE),
+        ((A, C_, B_, DX, DC, WS, -16, 2, 64, 64, 16, F32), SIZE),
+        ((A, C_, B_, DX, DC, WS, 1 << 20, 2, 64, 64, 12, F32), SIZE),
+        ((A, C_, B_, DX, DC, WS, 1 << 20, 2, 64, 48, 32, F32), SHAPE),
+        ((A, C_, B_, DX, DC, WS, 1 << 20, 2, 64, 64, 16, 7), DTYPE),
+        ((A, C_, B_, DX, DC, 0x600004, 1 << 20, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, DX, DC, 0x500000 + 512, 1 << 20, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, DX, DC, 0x100000 - 256, 1 << 20, 2, 64, 64, 16, BF16), ALIAS),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
+def _det_workspace():
+    # the size query of circulant_bwd_det (its last argument is the output
+    # pointer); only failing cases, which write nothing through it
+    f = "circulant_bwd_det_workspace"
+    cases = [
+        ((2, 64, 64, 16, 1, None), NULL),
+        ((2, 64, 64, 12, 1, B_), SIZE),
+        ((2, 64, 64, 8192, 0, B_), SIZE),
+        ((-1, 64, 64, 16, 1, B_), SIZE),
+        ((2, 60, 64, 16, 1, B_), SHAPE),
+        ((I64_MAX, 4096, 4096, 4096, 1, B_), SIZE),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
 def _spectrum(fn):
     # argument order: (source, destination, ...): packed then spec for unpack, spec then packed for pack
     cases = [((A, B_, 0, 512, F32), OK), ((None, B_, 4, 512, F32), NULL), ((A, None, 4, 512, BF16), NULL)]
@@ -135,5 +172,5 @@ def _rdfft2d(fn):
 
 
 CASES = (_rdfft("rdfft_forward") + _rdfft("rdfft_inverse") + _circ_fwd() + _circ_bwd() + _circ_fwd_zero()
-         + _circ_bwd_acc() + _spectrum("rdfft_unpack")
+         + _circ_bwd_acc() + _circ_bwd_det() + _det_workspace() + _spectrum("rdfft_unpack")
          + _spectrum("rdfft_pack") + _rdfft2d("rdfft2d_forward") + _rdfft2d("rdfft2d_inverse"))

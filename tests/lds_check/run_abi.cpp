@@ -8,6 +8,9 @@
 //   run_abi pack       <rows> <p> <dtype> <spec> <packed>
 //   run_abi circ_fwd   <batch> <d_in> <d_out> <p> <dtype> <x> <c> <y>
 //   run_abi circ_bwd   <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <dx|-> <dc|->
+//   run_abi circ_det   <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <dx|-> <dc>
+//                      (circulant_bwd_det with a workspace of the size its query
+//                      gives, filled with garbage; dc filled with garbage too)
 //   run_abi circ_step  <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <y> <dx|-> <dc>
 //                      (circulant_fwd_zero into a dc that holds garbage, then
 //                      circulant_bwd_acc twice: dc = 2 x the gradient)
@@ -110,6 +113,13 @@ int call_case(const std::string& line) {
   if (f == "circulant_bwd_acc" && n == 10)
     return circulant_bwd_acc(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
                              num(6), num(7), num(8), num(9), int(num(10)), nullptr);
+  if (f == "circulant_bwd_det" && n == 12)
+    return circulant_bwd_det(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
+                             static_cast<float*>(ptr(6)), num(7), num(8), num(9), num(10), num(11), int(num(12)),
+                             nullptr);
+  if (f == "circulant_bwd_det_workspace" && n == 6)
+    return circulant_bwd_det_workspace(num(1), num(2), num(3), num(4), int(num(5)),
+                                       static_cast<int64_t*>(ptr(6)));
   if (f == "circulant_bwd" && n == 10)
     return circulant_bwd(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
                          num(6), num(7), num(8), num(9), int(num(10)), nullptr);
@@ -172,6 +182,26 @@ int main(int argc, char** argv) {
                        want_dc ? static_cast<float*>(dc.p) : nullptr, b, di, dout, p, dt, nullptr);
     if (want_dx) write_file(argv[10], dx);
     if (want_dc) write_file(argv[11], dc);
+  } else if (op == "circ_det" && argc == 12) {
+    const int64_t b = arg(argv, 2), di = arg(argv, 3), dout = arg(argv, 4), p = arg(argv, 5);
+    const int dt = static_cast<int>(arg(argv, 6));
+    Buf x = read_file(argv[7], b * di * esize(dt));
+    Buf c = read_file(argv[8], (dout / p) * di * 4);
+    Buf dy = read_file(argv[9], b * dout * esize(dt));
+    const bool want_dx = std::strcmp(argv[10], "-") != 0;
+    int64_t need = 0;
+    st = circulant_bwd_det_workspace(b, di, dout, p, want_dx ? 1 : 0, &need);
+    if (st == RDFFT_OK) {
+      Buf ws = alloc(static_cast<size_t>(need));
+      for (size_t i = 0; i < ws.n / 4; ++i) static_cast<float*>(ws.p)[i] = -777.0f;
+      Buf dx = alloc(b * di * esize(dt));
+      Buf dc = alloc((dout / p) * di * 4);
+      for (size_t i = 0; i < dc.n / 4; ++i) static_cast<float*>(dc.p)[i] = 12345.0f;
+      st = circulant_bwd_det(x.p, static_cast<const float*>(c.p), dy.p, want_dx ? dx.p : nullptr,
+                             static_cast<float*>(dc.p), static_cast<float*>(ws.p), need, b, di, dout, p, dt, nullptr);
+      if (want_dx) write_file(argv[10], dx);
+      write_file(argv[11], dc);
+    }
   } else if (op == "circ_step" && argc == 13) {
     const int64_t b = arg(argv, 2), di = arg(argv, 3), dout = arg(argv, 4), p = arg(argv, 5);
     const int dt = static_cast<int>(arg(argv, 6));

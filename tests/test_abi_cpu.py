@@ -41,6 +41,7 @@ def test_exports_every_declared_symbol(L):
     names = _header_functions()
     assert set(names) == {"rdfft_abi_version", "rdfft_status_string", "rdfft_forward", "rdfft_inverse",
                           "circulant_fwd", "circulant_bwd", "circulant_fwd_zero", "circulant_bwd_acc",
+                          "circulant_bwd_det", "circulant_bwd_det_workspace",
                           "rdfft_unpack", "rdfft_pack",
                           "rdfft2d_forward", "rdfft2d_inverse"}
     for n in names:
@@ -72,13 +73,20 @@ def test_case_constants_match_header():
                          ids=[f"{c[0]}-{i}" for i, c in enumerate(abi_cases.CASES)])
 def test_validation(L, fn, args, want):
     f = getattr(L, fn)
-    # pointer positions: every argument before the first size is a pointer
+    # pointer positions: the leading arguments (and, for the workspace query,
+    # its last one); circulant_bwd_det's seventh is the workspace size
     n_ptr = {"rdfft_forward": 1, "rdfft_inverse": 1, "circulant_fwd": 3, "circulant_bwd": 5,
-             "circulant_fwd_zero": 4, "circulant_bwd_acc": 5, "rdfft_unpack": 2,
+             "circulant_fwd_zero": 4, "circulant_bwd_acc": 5, "circulant_bwd_det": 6,
+             "circulant_bwd_det_workspace": 0, "rdfft_unpack": 2,
              "rdfft_pack": 2, "rdfft2d_forward": 1, "rdfft2d_inverse": 1}[fn]
-    cargs = [ctypes.c_void_p(a) if i < n_ptr and a is not None else (None if i < n_ptr else a)
-             for i, a in enumerate(args)]
-    assert f(*cargs, None) == STATUS[want]
+    ptrs = set(range(n_ptr)) | ({len(args) - 1} if fn == "circulant_bwd_det_workspace" else set())
+    cargs = [(ctypes.c_void_p(a) if a is not None else None) if i in ptrs else a for i, a in enumerate(args)]
+    if fn == "circulant_bwd_det_workspace":  # an int64_t* output, no stream argument
+        out = args[-1]
+        cargs[-1] = ctypes.cast(out, ctypes.POINTER(ctypes.c_int64)) if out is not None else None
+        assert f(*cargs) == STATUS[want]
+    else:
+        assert f(*cargs, None) == STATUS[want]
 
 
 def test_binding_refuses_cpu_tensors():

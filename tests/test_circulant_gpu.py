@@ -183,6 +183,48 @@ def test_zeroing_forward_and_accumulating_backward(batch, d_in, d_out, p, dtype,
     assert row_relerr(to_f64(dc).reshape(-1, p), 2 * dco.reshape(-1, p)) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("batch,d_in,d_out,p,dtype,want_dx", [
+    (33, 256, 128, 16, "f32", True), (70, 1024, 2048, 64, "f16", False), (96, 2048, 2048, 512, "f32", False),
+    (256, 4096, 4096, 128, "bf16", True), (2048, 4096, 4096, 1024, "bf16", True), (256, 4096, 4096, 4096, "bf16", True)])
+def test_deterministic_dc(batch, d_in, d_out, p, dtype, want_dx):
+    """circulant_bwd_det: ten calls give bitwise the same dc, whatever the
+    workspace held before (NaN here); dx is circulant_bwd's bit for bit; dc
+    matches the oracle and the atomically summed dc of circulant_bwd to
+    rounding.  Routes: small p, dc alone with packed-spectra and time-domain
+    slices, and the one-launch backward (D=4096 at p = 128, 1024, 4096)."""
+    q, k = d_out // p, d_in // p
+    x, xr = device_input((batch, d_in), syn.WL_TEST, syn.T_X, p + 7, dtype=dtype)
+    c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, p + 7, scale=d_in**-0.5, dtype="f32")
+    dy, dyr = device_input((batch, d_out), syn.WL_TEST, syn.T_DY, p + 7, dtype=dtype)
+    _say(f"deterministic dc B={batch} d_in={d_in} d_out={d_out} p={p} {dtype} dx={want_dx}")
+    need = bcl.circulant_bwd_det_workspace(batch, d_in, d_out, p, want_dx)
+    ws = torch.empty(need // 4, dtype=torch.float32, device="cuda:0")
+    dx_ref, dc_ref = bcl.circulant_bwd(x, c, dy, need_dx=want_dx)
+    runs = []
+    for _ in range(10):
+        ws.fill_(float("nan"))
+        runs.append(bcl.circulant_bwd_det(x, c, dy, ws=ws, need_dx=want_dx))
+    torch.cuda.synchronize()
+    dx0, dc0 = runs[0]
+    for dx, dc in runs:
+        assert torch.equal(dc, dc0)
+        if want_dx:
+            assert torch.equal(dx, dx_ref)
+    dxo, dco = co.circulant_backward_fft(xr, cr, dyr)
+    assert row_relerr(to_f64(dc0).reshape(-1, p), dco.reshape(-1, p)) <= TOL["f32"]
+    assert row_relerr(to_f64(dc0).reshape(-1, p), to_f64(dc_ref).reshape(-1, p)) <= 1e-6
+    if want_dx:
+        assert row_relerr(to_f64(dx0), dxo) <= TOL[dtype]
+    # a workspace one float short is refused, with nothing written
+    if need >= 4:
+        short = torch.empty(need // 4 - 1, dtype=torch.float32, device="cuda:0")
+        dc_keep = torch.full_like(c, 7.0)
+        with pytest.raises(bcl.RdfftError):
+            bcl.circulant_bwd_det(x, c, dy, dc=dc_keep, ws=short, need_dx=want_dx)
+        torch.cuda.synchronize()
+        assert torch.all(dc_keep == 7.0)
+
+
 def test_empty_batch():
     c = torch.randn(2, 2, 16, device="cuda:0")
     x = torch.empty(0, 32, device="cuda:0")

@@ -99,6 +99,29 @@ def test_training_step_graph_replays(b, d, p, want_dx):
         assert err <= 1e-5, (i, err)
 
 
+@pytest.mark.parametrize("b,d,p,want_dx", [(64, 1024, 128, True), (24, 256, 16, True), (40, 512, 64, False)])
+def test_deterministic_dc_graph_replays(b, d, p, want_dx):
+    # circulant_bwd_det captured: every replay gives the eager result bit for bit
+    x, _ = device_input((b, d), syn.WL_TEST, syn.T_X, 35, dtype="bf16")
+    c, _ = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 35, scale=1 / 32)
+    dy, _ = device_input((b, d), syn.WL_TEST, syn.T_DY, 35, dtype="bf16")
+    ws = torch.empty(bcl.circulant_bwd_det_workspace(b, d, d, p, want_dx) // 4, device="cuda:0")
+    dx0, dc0 = bcl.circulant_bwd_det(x, c, dy, ws=ws, need_dx=want_dx)
+    dc = torch.empty_like(dc0)
+    dx = torch.empty_like(x) if want_dx else None
+    g = _capture(lambda: bcl.circulant_bwd_det(x, c, dy, dx=dx, dc=dc, ws=ws, need_dx=want_dx))
+    for i in range(4):
+        for t in (dx, dc, ws):
+            if t is not None:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dc, dc0), i
+        if want_dx:
+            assert torch.equal(dx, dx0), i
+
+
 def test_2d_and_spectrum_graph_replays():
     x0, _ = device_input((2, 256, 512), syn.WL_TEST, syn.T_X, 33)
     eager = x0.clone()

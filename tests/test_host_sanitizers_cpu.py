@@ -113,6 +113,12 @@ def test_circulant_calls(exe, tmp_path, batch, d_in, d_out, p):
     dxo, dco = co.circulant_backward_dense(xr, cr, gr)
     assert _relerr(_read(fdx, (batch, d_in), "f32"), dxo) <= 1e-5
     assert _relerr(_read(fdc, (q * k, p), "f32"), dco.reshape(q * k, p)) <= 1e-5
+    # the deterministic dc (workspace slices summed in order)
+    r = subprocess.run([exe, "circ_det", *dims, fx, fc, fg, fdx, fdc], capture_output=True, text=True, env=ENV,
+                       timeout=300)
+    _check_clean(r)
+    assert _relerr(_read(fdx, (batch, d_in), "f32"), dxo) <= 1e-5
+    assert _relerr(_read(fdc, (q * k, p), "f32"), dco.reshape(q * k, p)) <= 1e-5
     # the zeroing forward and the accumulating backward (twice)
     r = subprocess.run([exe, "circ_step", *dims, fx, fc, fg, fy, fdx, fdc], capture_output=True, text=True, env=ENV,
                        timeout=300)

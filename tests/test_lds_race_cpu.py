@@ -165,6 +165,32 @@ def test_circulant_step(exe, tmp_path, batch, d_in, d_out, p, dt, want_dx):
     assert _relerr(_read(fdc, (q * k, p), "f32"), 2 * dco.reshape(q * k, p)) <= TOL["f32"]
 
 
+# the deterministic dc (workspace slices summed in order) on every route:
+# small-p kernels, token-persistent dc alone with packed-spectra slices (p = 64,
+# 128) and time-domain slices (p = 256), and the one-launch backward with dx
+DET_CASES = [(5, 64, 48, 16, "f32", True), (4, 96, 64, 32, "f32", False), (7, 256, 192, 64, "bf16", False),
+             (9, 512, 512, 128, "bf16", False), (5, 512, 1024, 256, "f32", False), (9, 512, 512, 128, "bf16", True),
+             (5, 2048, 4096, 1024, "bf16", True), (5, 4096, 4096, 4096, "bf16", True)]
+
+
+@pytest.mark.parametrize("batch,d_in,d_out,p,dt,want_dx", DET_CASES)
+def test_circulant_det(exe, tmp_path, batch, d_in, d_out, p, dt, want_dx):
+    q, k = d_out // p, d_in // p
+    xt, xr = syn.cast_like_device(syn.normal((batch, d_in), syn.WL_TEST, syn.T_X, 980 + p), dt)
+    ct, cr = syn.cast_like_device(syn.normal((q, k, p), syn.WL_TEST, syn.T_C, 980 + p, d_in**-0.5), "f32")
+    gt, gr = syn.cast_like_device(syn.normal((batch, d_out), syn.WL_TEST, syn.T_DY, 980 + p), dt)
+    fx, fc, fg = str(tmp_path / "x"), str(tmp_path / "c"), str(tmp_path / "dy")
+    fdx, fdc = str(tmp_path / "dx"), str(tmp_path / "dc")
+    _write(fx, xt)
+    _write(fc, ct)
+    _write(fg, gt)
+    _run(exe, "circ_det", batch, d_in, d_out, p, DT[dt], fx, fc, fg, fdx if want_dx else "-", fdc)
+    dxo, dco = co.circulant_backward_fft(xr, cr, gr)
+    if want_dx:
+        assert _relerr(_read(fdx, (batch, d_in), dt), dxo) <= TOL[dt]
+    assert _relerr(_read(fdc, (q * k, p), "f32"), dco.reshape(q * k, p)) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("n,h,w,dt", [(2, 16, 32, "f32"), (1, 64, 512, "bf16"), (1, 4096, 16, "f32"),
                                       (1, 512, 64, "f16"), (3, 8, 8, "f32")])
 def test_2d(exe, tmp_path, n, h, w, dt):

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     circulant_bwd,
     circulant_bwd_acc,
     circulant_bwd_det,
+    circulant_bwd_det_noalloc,
     circulant_bwd_det_workspace,
     circulant_fwd,
     circulant_fwd_zero,

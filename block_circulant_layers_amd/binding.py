@@ -27,6 +27,7 @@ __all__ = [
     "circulant_bwd_acc",
     "circulant_bwd_det",
     "circulant_bwd_det_workspace",
+    "circulant_bwd_det_noalloc",
     "RDFFT_F32",
     "RDFFT_BF16",
     "RDFFT_F16",
@@ -58,6 +59,7 @@ SIGNATURES = {
     "circulant_bwd_det_workspace": (ctypes.c_int, [_I64, _I64, _I64, _I64, ctypes.c_int, ctypes.POINTER(_I64)]),
     "circulant_bwd_det": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
                                          _VP]),
+    "circulant_bwd_det_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_unpack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_pack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft2d_forward": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
@@ -265,6 +267,25 @@ def circulant_bwd_det(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: to
     _call("circulant_bwd_det", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
           dx.data_ptr() if dx is not None else None, dc.data_ptr(), ws.data_ptr(), ws.numel() * 4,
           batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
+    return dx, dc
+
+
+def circulant_bwd_det_noalloc(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor,
+                              dc: torch.Tensor, stream=None):
+    """:func:`circulant_bwd_det` without a workspace argument, for callers that
+    cannot allocate: the library's 32 MiB per-GPU array serves as workspace.
+    dx (may be None) and dc must be given; nothing is allocated."""
+    q, k, p, batch = _circ_dims(x, c)
+    _check_gpu(x, c, dy, dx, dc)
+    if dy.dtype != x.dtype or (dx is not None and dx.dtype != x.dtype):
+        raise ValueError("dy and dx must have the dtype of x")
+    if dy.numel() != batch * q * p:
+        raise ValueError("dy must have shape (..., d_out)")
+    if dc.dtype != torch.float32 or dc.shape != c.shape:
+        raise ValueError("dc must be float32 with the shape of c")
+    _call("circulant_bwd_det_noalloc", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
+          dx.data_ptr() if dx is not None else None, dc.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
+          _stream(x, stream))
     return dx, dc
 
 

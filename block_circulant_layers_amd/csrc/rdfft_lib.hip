@@ -1,6 +1,8 @@
 // rdfft_lib.hip -- C ABI of librdfft.so: argument checks, kernel selection, launches.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "rdfft.h"
 #include "rdfft_kernels.hpp"
 #include "circulant_kernels.hpp"
@@ -413,6 +415,32 @@ inline int64_t dc_token_ranges_dispatch(int64_t batch, int64_t d_in, int64_t d_o
 #undef CALL
 }
 
+// ---- the allocation-free deterministic backward ---------------------------
+// Workspace of circulant_bwd_det_noalloc: a file-scope device array, one copy
+// on every GPU the library runs on, held until the process ends.  Host code
+// never passes its name to a kernel (on the host the name stands for a host
+// stand-in); it takes the array's device address once per device with
+// hipGetSymbolAddress and passes that.
+constexpr int64_t kScratchBytes = int64_t{32} << 20;  // 32 MiB
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+// device address of the current device's scratch, resolved on the first call
+// on that device; nullptr when the runtime cannot resolve it
+float* scratch_ptr() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<float*> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  float* p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+    p = static_cast<float*>(addr);
+    cached[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 // bytes of a deterministic dc's workspace: one q k p slice of floats per token range
 inline int circ_det_workspace(int64_t batch, int64_t d_in, int64_t d_out, int64_t p, bool with_dx, int64_t* bytes) {
   const int64_t ranges = dc_token_ranges_dispatch(batch, d_in, d_out, p, with_dx);
@@ -545,6 +573,9 @@ const char* rdfft_status_string(int status) {
     case RDFFT_ERR_ALIGN: return "pointer not 16-byte aligned";
     case RDFFT_ERR_ALIAS: return "output buffer overlaps another buffer";
     case RDFFT_ERR_LAUNCH: return "kernel launch failed";
+    case RDFFT_ERR_SCRATCH:
+      return "the deterministic dc of this shape needs more than the 32 MiB workspace of the allocation-free call "
+             "(use circulant_bwd_det with a workspace)";
     default: return "unknown status";
   }
 }
@@ -614,6 +645,26 @@ int circulant_bwd_det(const void* x, const float* c, const void* dy, void* dx, f
   if (st != RDFFT_OK) return st;
   st = rdfft::check_det_workspace(x, c, dy, dx, dc, ws, ws_bytes, need, batch, d_in, d_out, p, dtype);
   if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, false, s, ws);
+  });
+}
+
+int circulant_bwd_det_noalloc(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
+                              int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream) {
+  int st = rdfft::check_circulant_bwd(x, c, dy, dx, dc, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  if (dc == nullptr) return RDFFT_ERR_NULL;
+  int64_t need = 0;
+  st = rdfft::circ_det_workspace(batch, d_in, d_out, p, dx != nullptr, &need);
+  if (st != RDFFT_OK) return st;
+  if (need > rdfft::kScratchBytes) return RDFFT_ERR_SCRATCH;
+  float* ws = nullptr;
+  if (need > 0) {
+    ws = rdfft::scratch_ptr();
+    if (ws == nullptr) return RDFFT_ERR_LAUNCH;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return rdfft::by_dtype(dtype, [&](auto io) {
     return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, false, s, ws);

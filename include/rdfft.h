@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RDFFT_ABI_VERSION 4
+#define RDFFT_ABI_VERSION 5
 
 /* storage types */
 #define RDFFT_F32 0
@@ -60,6 +60,7 @@ extern "C" {
 #define RDFFT_ERR_ALIGN 5  /* a pointer is not 16-byte aligned */
 #define RDFFT_ERR_ALIAS 6  /* an output buffer overlaps another buffer of the call */
 #define RDFFT_ERR_LAUNCH 7 /* the HIP runtime refused a kernel launch */
+#define RDFFT_ERR_SCRATCH 8 /* circulant_bwd_det_noalloc: the shape needs more than its 32 MiB workspace */
 
 /* Version of this ABI (RDFFT_ABI_VERSION of the library that was built). */
 int rdfft_abi_version(void);
@@ -177,6 +178,25 @@ int circulant_bwd_det_workspace(int64_t batch, int64_t d_in, int64_t d_out, int6
  */
 int circulant_bwd_det(const void* x, const float* c, const void* dy, void* dx, float* dc, float* ws, int64_t ws_bytes,
                       int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_bwd_det_noalloc -- circulant_bwd_det for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and the same bitwise
+ * result, with the workspace taken from a 32 MiB array the library holds on
+ * every GPU it runs on until the process ends.  Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library call.  Arguments as
+ * circulant_bwd_det without ws / ws_bytes.
+ *   - Returns RDFFT_ERR_SCRATCH, touching nothing, when the shape needs more
+ *     than 32 MiB (circulant_bwd_det_workspace gives the need).
+ *   - All calls on one GPU share that GPU's array, which keeps the last call's
+ *     contents; no call needs it cleared (every slice a call reads, it wrote).
+ *     Calls that overlap on one GPU (other streams, other threads) race on it:
+ *     order them on one stream.
+ *   - The array's device address is looked up on the first call on each device.
+ */
+int circulant_bwd_det_noalloc(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
+                              int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
 
 /*
  * rdfft_unpack -- packed spectra to explicit complex bins (the packed layout

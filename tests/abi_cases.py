@@ -9,6 +9,7 @@ build of the library under AddressSanitizer and UndefinedBehaviorSanitizer.
 """
 
 OK, NULL, SIZE, SHAPE, DTYPE, ALIGN, ALIAS = "OK", "NULL", "SIZE", "SHAPE", "DTYPE", "ALIGN", "ALIAS"
+SCRATCH = "SCRATCH"
 F32, BF16, F16 = 0, 1, 2
 A, B_, C_ = 0x100000, 0x200000, 0x300000
 DX, DC = 0x400000, 0x500000
@@ -137,6 +138,25 @@ def _circ_bwd_det():
     return [(f, a, e) for a, e in cases]
 
 
+def _circ_bwd_det_noalloc():
+    # circulant_bwd's checks, dc required, and the 32 MiB limit of the
+    # library's own workspace: at p = 16, 65536 x 65536 features the dc slices
+    # alone need 1 GiB (buffers 1 TiB apart so that none overlaps another)
+    f = "circulant_bwd_det_noalloc"
+    T = 1 << 40
+    cases = [
+        ((A, C_, B_, DX, None, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, None, None, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, 2, 64, 64, 12, F32), SIZE),
+        ((A, C_, B_, DX, DC, 2, 64, 64, 16, 5), DTYPE),
+        ((A, C_, B_, DX, 0x500004, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, DX, 0x300000 + 16, 2, 64, 64, 16, F32), ALIAS),
+        ((T, 2 * T, 3 * T, 4 * T, 5 * T, 256, 65536, 65536, 16, F32), SCRATCH),
+        ((T, 2 * T, 3 * T, None, 5 * T, 256, 65536, 65536, 16, BF16), SCRATCH),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
 def _det_workspace():
     # the size query of circulant_bwd_det (its last argument is the output
     # pointer); only failing cases, which write nothing through it
@@ -172,5 +192,5 @@ def _rdfft2d(fn):
 
 
 CASES = (_rdfft("rdfft_forward") + _rdfft("rdfft_inverse") + _circ_fwd() + _circ_bwd() + _circ_fwd_zero()
-         + _circ_bwd_acc() + _circ_bwd_det() + _det_workspace() + _spectrum("rdfft_unpack")
+         + _circ_bwd_acc() + _circ_bwd_det() + _circ_bwd_det_noalloc() + _det_workspace() + _spectrum("rdfft_unpack")
          + _spectrum("rdfft_pack") + _rdfft2d("rdfft2d_forward") + _rdfft2d("rdfft2d_inverse"))

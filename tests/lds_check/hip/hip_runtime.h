@@ -32,6 +32,8 @@
 #define __global__
 #define __device__
 #define __host__
+#define __align__(x) __attribute__((aligned(x)))
+#define HIP_SYMBOL(X) X
 #define __forceinline__ inline
 #define __launch_bounds__(...)
 #define __shared__ static
@@ -172,6 +174,12 @@ inline float unsafeAtomicAdd(float* p, float v) {
 }
 
 inline hipError_t hipGetLastError() { return hipSuccess; }
+// a __device__ variable is a host variable here: its address is the symbol's
+template <class T>
+inline hipError_t hipGetSymbolAddress(void** p, const T& symbol) {
+  *p = const_cast<void*>(static_cast<const void*>(&symbol));
+  return hipSuccess;
+}
 inline hipError_t hipGetDevice(int* d) {
   *d = 0;
   return hipSuccess;

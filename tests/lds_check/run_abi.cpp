@@ -117,6 +117,10 @@ int call_case(const std::string& line) {
     return circulant_bwd_det(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
                              static_cast<float*>(ptr(6)), num(7), num(8), num(9), num(10), num(11), int(num(12)),
                              nullptr);
+  if (f == "circulant_bwd_det_noalloc" && n == 10)
+    return circulant_bwd_det_noalloc(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4),
+                                     static_cast<float*>(ptr(5)), num(6), num(7), num(8), num(9), int(num(10)),
+                                     nullptr);
   if (f == "circulant_bwd_det_workspace" && n == 6)
     return circulant_bwd_det_workspace(num(1), num(2), num(3), num(4), int(num(5)),
                                        static_cast<int64_t*>(ptr(6)));

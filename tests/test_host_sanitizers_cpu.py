@@ -35,7 +35,7 @@ def _status_codes():
     d = {k: int(v) for k, v in re.findall(r"#define\s+(RDFFT_\w+)\s+(\d+)", hdr)}
     return {"OK": d["RDFFT_OK"], "NULL": d["RDFFT_ERR_NULL"], "SIZE": d["RDFFT_ERR_SIZE"],
             "SHAPE": d["RDFFT_ERR_SHAPE"], "DTYPE": d["RDFFT_ERR_DTYPE"], "ALIGN": d["RDFFT_ERR_ALIGN"],
-            "ALIAS": d["RDFFT_ERR_ALIAS"]}
+            "ALIAS": d["RDFFT_ERR_ALIAS"], "SCRATCH": d["RDFFT_ERR_SCRATCH"]}
 
 
 @pytest.fixture(scope="module")

@@ -27,6 +27,7 @@ The JSON line also carries
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -437,6 +438,9 @@ def bench_layer_memory(batch, d, p, form="rdfft_layer"):
     the step needed beyond those tensors (workspace).  ``form`` picks this
     library's layer or one of the torch.fft forms run as context."""
     fn = LAYER_FORMS[form]
+    # earlier workloads' buffers held in reference cycles (a setup dict and
+    # the step closure that refers to it) must not be freed inside the count
+    gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     base = torch.cuda.memory_allocated()
@@ -539,11 +543,12 @@ def circ_algorithmic(batch, d, p, eb):
     return nbytes, flops
 
 
-def circ_layer_setup(batch, d, p, nrot=32):
+def circ_layer_setup(batch, d, p, nrot=32, spectra=False):
     """The single-layer workload as bench_circ_layer times it: nrot token
     batches (bf16), one c (fp32), and ``rot``, a rotation of nrot training
     steps.  After a rotation ys[j] and dxs[j] hold step j's outputs and dc the
-    last step's gradient."""
+    last step's gradient.  spectra: the steps keep the weight spectra in
+    cs (circulant_fwd_step writes them, circulant_bwd_spec reads them)."""
     q = k = d // p
     w = {"xs": [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, i, dtype=torch.bfloat16) for i in range(nrot)],
          "dys": [syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, i, dtype=torch.bfloat16)
@@ -552,20 +557,25 @@ def circ_layer_setup(batch, d, p, nrot=32):
     w["ys"] = [torch.empty_like(x) for x in w["xs"]]
     w["dxs"] = [torch.empty_like(x) for x in w["xs"]]
     w["dc"] = torch.empty_like(w["c"])
+    w["cs"] = torch.empty_like(w["c"])
 
     def rot():
         # a training step of the layer: the forward clears dc in its launch,
         # the backward adds the token sum into it (two launches per step)
         for j in range(nrot):
-            bcl.circulant_fwd_zero(w["xs"][j], w["c"], w["dc"], w["ys"][j])
-            bcl.circulant_bwd_acc(w["xs"][j], w["c"], w["dys"][j], w["dc"], dx=w["dxs"][j])
+            if spectra:
+                bcl.circulant_fwd_step(w["xs"][j], w["c"], w["cs"], w["ys"][j], dc=w["dc"])
+                bcl.circulant_bwd_spec(w["xs"][j], w["cs"], w["dys"][j], dx=w["dxs"][j], dc=w["dc"], accumulate=True)
+            else:
+                bcl.circulant_fwd_zero(w["xs"][j], w["c"], w["dc"], w["ys"][j])
+                bcl.circulant_bwd_acc(w["xs"][j], w["c"], w["dys"][j], w["dc"], dx=w["dxs"][j])
 
     w["rot"] = rot
     return w
 
 
-def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
-    w = circ_layer_setup(batch, d, p, nrot)  # kept alive: the graph holds raw pointers into it
+def bench_circ_layer(batch, d, p, steps, warmup, nrot=32, spectra=False):
+    w = circ_layer_setup(batch, d, p, nrot, spectra)  # kept alive: the graph holds raw pointers into it
     g = _graph(w["rot"])
     for _ in range(max(1, -(-warmup // nrot))):
         g.replay()
@@ -587,10 +597,11 @@ def bench_circ_layer(batch, d, p, steps, warmup, nrot=32):
     }
 
 
-def circ_adapters_setup(n_adapters=128, batch=2048, d=4096, p=1024):
+def circ_adapters_setup(n_adapters=128, batch=2048, d=4096, p=1024, spectra=False):
     """The adapter workload as bench_circ_adapters times it: per adapter a
     token batch, an upstream gradient (bf16) and c (fp32), and ``step``: the
-    forwards of all adapters in order, then the backwards in reverse."""
+    forwards of all adapters in order, then the backwards in reverse.
+    spectra: each adapter keeps its weight spectra from forward to backward."""
     q = k = d // p
     w = {"xs": [syn.torch_normal((batch, d), syn.WL_CIRC_ADAPTERS, syn.T_X, a, dtype=torch.bfloat16)
                 for a in range(n_adapters)],
@@ -600,19 +611,27 @@ def circ_adapters_setup(n_adapters=128, batch=2048, d=4096, p=1024):
     w["ys"] = [torch.empty_like(x) for x in w["xs"]]
     w["dxs"] = [torch.empty_like(x) for x in w["xs"]]
     w["dcs"] = [torch.empty_like(c) for c in w["cs"]]
+    w["specs"] = [torch.empty_like(c) for c in w["cs"]] if spectra else None
 
     def step():
         for a in range(n_adapters):
-            bcl.circulant_fwd_zero(w["xs"][a], w["cs"][a], w["dcs"][a], w["ys"][a])
+            if spectra:
+                bcl.circulant_fwd_step(w["xs"][a], w["cs"][a], w["specs"][a], w["ys"][a], dc=w["dcs"][a])
+            else:
+                bcl.circulant_fwd_zero(w["xs"][a], w["cs"][a], w["dcs"][a], w["ys"][a])
         for a in reversed(range(n_adapters)):
-            bcl.circulant_bwd_acc(w["xs"][a], w["cs"][a], w["dys"][a], w["dcs"][a], dx=w["dxs"][a])
+            if spectra:
+                bcl.circulant_bwd_spec(w["xs"][a], w["specs"][a], w["dys"][a], dx=w["dxs"][a], dc=w["dcs"][a],
+                                       accumulate=True)
+            else:
+                bcl.circulant_bwd_acc(w["xs"][a], w["cs"][a], w["dys"][a], w["dcs"][a], dx=w["dxs"][a])
 
     w["step"] = step
     return w
 
 
-def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=1024):
-    w = circ_adapters_setup(n_adapters, batch, d, p)  # kept alive: the graph holds raw pointers into it
+def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=1024, spectra=False):
+    w = circ_adapters_setup(n_adapters, batch, d, p, spectra)  # kept alive: the graph holds raw pointers into it
     g = _graph(w["step"])
     for _ in range(warmup):
         g.replay()
@@ -633,6 +652,34 @@ def bench_circ_adapters(steps, warmup, n_adapters=128, batch=2048, d=4096, p=102
         "roofline_ms": round(t_roof, 4),
         "frac_of_roofline": round(t_roof / ms, 4),
     }
+
+
+def bench_circ_forward_fixed(batch, d, p, spectra, steps=256, warmup=32, nrot=32):
+    """Forwards only, with c fixed (inference): nrot token batches in rotation,
+    from c (circulant_fwd) or from its spectra computed once beforehand
+    (circulant_fwd_spec, the spectra launch outside the timed region)."""
+    w = circ_layer_setup(batch, d, p, nrot)  # kept alive: the graph holds raw pointers into it
+    bcl.circulant_weight_spectra(w["c"], w["cs"])
+
+    def rot():
+        for j in range(nrot):
+            if spectra:
+                bcl.circulant_fwd_spec(w["xs"][j], w["cs"], w["ys"][j])
+            else:
+                bcl.circulant_fwd(w["xs"][j], w["c"], w["ys"][j])
+
+    g = _graph(rot)
+    for _ in range(max(1, -(-warmup // nrot))):
+        g.replay()
+    reps = max(1, -(-steps // nrot))
+    tm = Timer()
+    torch.cuda.synchronize()
+    hold_gpu(1.0)
+    tm.start()
+    for _ in range(reps):
+        g.replay()
+    ms = tm.stop() / (reps * nrot)
+    return {"tokens_per_s": round(batch / (ms * 1e-3), 1), "ms_per_forward": round(ms, 5)}
 
 
 def profile_circulant(reps=3):
@@ -1080,6 +1127,13 @@ def main():
         for pp in (128, 512, 4096):
             log(f"extra: circulant layer D=4096 B=256 p={pp}")
             extra[f"circulant_d4096_b256_p{pp}_bf16"] = bench_circ_layer(256, 4096, pp, 256, 32)
+            log(f"extra: circulant layer D=4096 B=256 p={pp}, weight spectra kept from forward to backward")
+            extra[f"circulant_d4096_b256_p{pp}_bf16_weight_spectra"] = bench_circ_layer(256, 4096, pp, 256, 32,
+                                                                                        spectra=True)
+            log(f"extra: circulant forward D=4096 B=256 p={pp}, fixed weights, from c and from its spectra")
+            extra[f"circulant_d4096_b256_p{pp}_bf16_forward_fixed_weights"] = {
+                "from_c": bench_circ_forward_fixed(256, 4096, pp, False),
+                "from_spectra": bench_circ_forward_fixed(256, 4096, pp, True)}
         log("extra: single-layer peak memory")
         mem = {}
         for (b, d, pp) in ((1, 4096, 128), (1, 4096, 512), (1, 4096, 1024), (1, 4096, 4096), (256, 4096, 128),
@@ -1100,6 +1154,9 @@ def main():
         extra["torch_fft_context"] = ctx
         log("extra: 128 circulant adapters 4096x4096 p=1024, 2048 tokens")
         extra["circulant_128_adapters_d4096_p1024_b2048_bf16"] = bench_circ_adapters(10, 2)
+        log("extra: 128 circulant adapters, weight spectra kept from forward to backward")
+        extra["circulant_128_adapters_d4096_p1024_b2048_bf16_weight_spectra"] = bench_circ_adapters(10, 2,
+                                                                                                   spectra=True)
         out["extra"] = extra
         # The pages' own operator timings (Paper-Notes page, "实验关键数据";
         # hardware, batch and precision unstated there), beside this run's

@@ -15,8 +15,12 @@ from .binding import (  # noqa: F401
     circulant_bwd_det,
     circulant_bwd_det_noalloc,
     circulant_bwd_det_workspace,
+    circulant_bwd_spec,
     circulant_fwd,
+    circulant_fwd_spec,
+    circulant_fwd_step,
     circulant_fwd_zero,
+    circulant_weight_spectra,
     lib,
     lib_path,
     rdfft2d_forward,

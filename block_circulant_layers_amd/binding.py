@@ -28,6 +28,10 @@ __all__ = [
     "circulant_bwd_det",
     "circulant_bwd_det_workspace",
     "circulant_bwd_det_noalloc",
+    "circulant_weight_spectra",
+    "circulant_fwd_step",
+    "circulant_fwd_spec",
+    "circulant_bwd_spec",
     "RDFFT_F32",
     "RDFFT_BF16",
     "RDFFT_F16",
@@ -60,6 +64,11 @@ SIGNATURES = {
     "circulant_bwd_det": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
                                          _VP]),
     "circulant_bwd_det_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_weight_spectra": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP]),
+    "circulant_fwd_step": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_fwd_spec": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "circulant_bwd_spec": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_int, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                          _VP]),
     "rdfft_unpack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft_pack": (ctypes.c_int, [_VP, _VP, _I64, _I64, ctypes.c_int, _VP]),
     "rdfft2d_forward": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
@@ -286,6 +295,85 @@ def circulant_bwd_det_noalloc(x: torch.Tensor, c: torch.Tensor, dy: torch.Tensor
     _call("circulant_bwd_det_noalloc", x.device, x.data_ptr(), c.data_ptr(), dy.data_ptr(),
           dx.data_ptr() if dx is not None else None, dc.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
           _stream(x, stream))
+    return dx, dc
+
+
+def circulant_weight_spectra(c: torch.Tensor, cs: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """cs = the packed spectra of the weight rows c (float32, shape (q, k, p)),
+    the weights of :func:`circulant_fwd_spec` and :func:`circulant_bwd_spec`;
+    returns cs (allocated if None)."""
+    if c.dim() != 3 or c.dtype != torch.float32:
+        raise ValueError("c must be a float32 tensor of shape (q, k, p)")
+    q, k, p = c.shape
+    if cs is None:
+        cs = torch.empty_like(c)
+    _check_gpu(c, cs)
+    if cs.dtype != torch.float32 or cs.shape != c.shape:
+        raise ValueError("cs must be float32 with the shape of c")
+    _call("circulant_weight_spectra", c.device, c.data_ptr(), cs.data_ptr(), k * p, q * p, p, _stream(c, stream))
+    return cs
+
+
+def circulant_fwd_step(x: torch.Tensor, c: torch.Tensor, cs: torch.Tensor, y: torch.Tensor | None = None,
+                       dc: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """:func:`circulant_fwd` that also writes the weight spectra ``cs``
+    (float32, the shape of c) for :func:`circulant_bwd_spec`; a given ``dc``
+    is set to zero, as by :func:`circulant_fwd_zero`.  Returns y."""
+    q, k, p, batch = _circ_dims(x, c)
+    if y is None:
+        y = torch.empty(*x.shape[:-1], q * p, dtype=x.dtype, device=x.device)
+    _check_gpu(x, c, y, dc, cs)
+    if y.dtype != x.dtype:
+        raise ValueError("y must have the dtype of x")
+    for name, t in (("cs", cs), ("dc", dc)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != c.shape):
+            raise ValueError(f"{name} must be float32 with the shape of c")
+    _call("circulant_fwd_step", x.device, x.data_ptr(), c.data_ptr(), y.data_ptr(),
+          dc.data_ptr() if dc is not None else None, cs.data_ptr(), batch, k * p, q * p, p, _dtype_code(x),
+          _stream(x, stream))
+    return y
+
+
+def circulant_fwd_spec(x: torch.Tensor, cs: torch.Tensor, y: torch.Tensor | None = None,
+                       dc: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """:func:`circulant_fwd` from the weight spectra cs; a given ``dc``
+    (float32, the shape of cs) is also set to zero, as by
+    :func:`circulant_fwd_zero`.  Returns y."""
+    q, k, p, batch = _circ_dims(x, cs)
+    if y is None:
+        y = torch.empty(*x.shape[:-1], q * p, dtype=x.dtype, device=x.device)
+    _check_gpu(x, cs, y, dc)
+    if y.dtype != x.dtype:
+        raise ValueError("y must have the dtype of x")
+    if dc is not None and (dc.dtype != torch.float32 or dc.shape != cs.shape):
+        raise ValueError("dc must be float32 with the shape of cs")
+    _call("circulant_fwd_spec", x.device, x.data_ptr(), cs.data_ptr(), y.data_ptr(),
+          dc.data_ptr() if dc is not None else None, batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
+    return y
+
+
+def circulant_bwd_spec(x: torch.Tensor, cs: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor | None = None,
+                       dc: torch.Tensor | None = None, need_dx: bool = True, need_dc: bool = True,
+                       accumulate: bool = False, stream=None):
+    """:func:`circulant_bwd` (or, with ``accumulate``, :func:`circulant_bwd_acc`
+    into the given ``dc``) from the weight spectra cs; returns (dx, dc)."""
+    q, k, p, batch = _circ_dims(x, cs)
+    if need_dx and dx is None:
+        dx = torch.empty_like(x)
+    if accumulate and dc is None:
+        raise ValueError("accumulate needs the dc to add into")
+    if need_dc and dc is None:
+        dc = torch.empty_like(cs)
+    _check_gpu(x, cs, dy, dx, dc)
+    if dy.dtype != x.dtype or (dx is not None and dx.dtype != x.dtype):
+        raise ValueError("dy and dx must have the dtype of x")
+    if dy.numel() != batch * q * p:
+        raise ValueError("dy must have shape (..., d_out)")
+    if dc is not None and (dc.dtype != torch.float32 or dc.shape != cs.shape):
+        raise ValueError("dc must be float32 with the shape of cs")
+    _call("circulant_bwd_spec", x.device, x.data_ptr(), cs.data_ptr(), dy.data_ptr(),
+          dx.data_ptr() if dx is not None else None, dc.data_ptr() if dc is not None else None, int(bool(accumulate)),
+          batch, k * p, q * p, p, _dtype_code(x), _stream(x, stream))
     return dx, dc
 
 

@@ -84,7 +84,8 @@ int dispatch_rdfft(void* data, int64_t rows, int64_t p, hipStream_t s) {
 
 constexpr int kDcTargetWgs = 256;  // aim of the dc token split (workgroups in flight)
 
-template <int P, class Io>
+// WSPEC: c holds the weights' packed spectra (every launcher below)
+template <int P, class Io, bool WSPEC = false>
 int launch_circ_mm(const void* in, const float* c, void* out, int64_t batch, int64_t nin, int64_t nout, bool trans,
                    hipStream_t s) {
   constexpr MmParams K = mm_params(P);
@@ -94,9 +95,11 @@ int launch_circ_mm(const void* in, const float* c, void* out, int64_t batch, int
   const auto* pi = static_cast<const typename Io::T*>(in);
   auto* po = static_cast<typename Io::T*>(out);
   if (trans)
-    hipLaunchKernelGGL((circ_mm_kernel<P, true, Io>), grid, dim3(K.nt), 0, s, pi, c, po, batch, int(nin), int(nout));
+    hipLaunchKernelGGL((circ_mm_kernel<P, true, Io, WSPEC>), grid, dim3(K.nt), 0, s, pi, c, po, batch, int(nin),
+                       int(nout));
   else
-    hipLaunchKernelGGL((circ_mm_kernel<P, false, Io>), grid, dim3(K.nt), 0, s, pi, c, po, batch, int(nin), int(nout));
+    hipLaunchKernelGGL((circ_mm_kernel<P, false, Io, WSPEC>), grid, dim3(K.nt), 0, s, pi, c, po, batch, int(nin),
+                       int(nout));
   return launch_status();
 }
 
@@ -184,12 +187,14 @@ int64_t tokens_per_wg(int64_t batch, int64_t tiles, int tb, int64_t target = kTa
 
 // y = circulant product of `in` (forward, or transposed for dx).  When the
 // token-persistent kernel runs, it also clears zero[0..nzero) and sets
-// *zeroed; otherwise zero is left alone.
-template <int P, class Io>
+// *zeroed, and (forward from c) stores the weight spectra into wout if given;
+// otherwise zero and wout are left alone.
+template <int P, class Io, bool WSPEC = false>
 int launch_circ_product(const void* in, const float* c, void* out, int64_t batch, int64_t nin, int64_t nout, bool trans,
-                        hipStream_t s, float* zero = nullptr, int64_t nzero = 0, bool* zeroed = nullptr) {
+                        hipStream_t s, float* zero = nullptr, int64_t nzero = 0, bool* zeroed = nullptr,
+                        float* wout = nullptr, bool* wout_done = nullptr) {
   if constexpr (P >= 64) {
-    using S = TpShape<P>;
+    using S = TpShape<P, false, WSPEC>;
     if (nin <= S::CR && S::fits(static_cast<int>(nin)) && S::lds_bytes(static_cast<int>(nin)) <= kMaxLds &&
         nout <= 0x7fffffff) {
       const int64_t gy = (nout + S::K.to - 1) / S::K.to;
@@ -202,16 +207,17 @@ int launch_circ_product(const void* in, const float* c, void* out, int64_t batch
       auto* po = static_cast<typename Io::T*>(out);
       if (!zero) nzero = 0;
       if (trans)
-        hipLaunchKernelGGL((circ_tp_kernel<P, true, Io>), grid, dim3(S::K.nt), lds, s, pi, c, po, batch, int(nin),
-                           int(nout), tpw, zero, nzero);
+        hipLaunchKernelGGL((circ_tp_kernel<P, true, Io, WSPEC>), grid, dim3(S::K.nt), lds, s, pi, c, po, batch,
+                           int(nin), int(nout), tpw, zero, nzero, static_cast<float*>(nullptr));
       else
-        hipLaunchKernelGGL((circ_tp_kernel<P, false, Io>), grid, dim3(S::K.nt), lds, s, pi, c, po, batch, int(nin),
-                           int(nout), tpw, zero, nzero);
+        hipLaunchKernelGGL((circ_tp_kernel<P, false, Io, WSPEC>), grid, dim3(S::K.nt), lds, s, pi, c, po, batch,
+                           int(nin), int(nout), tpw, zero, nzero, WSPEC ? nullptr : wout);
       if (zeroed) *zeroed = nzero > 0;
+      if (wout_done) *wout_done = wout != nullptr && !trans && !WSPEC;
       return launch_status();
     }
   }
-  return launch_circ_mm<P, Io>(in, c, out, batch, nin, nout, trans, s);
+  return launch_circ_mm<P, Io, WSPEC>(in, c, out, batch, nin, nout, trans, s);
 }
 
 // split of the token-persistent weight-gradient tiles, `target` workgroups aimed at
@@ -270,10 +276,10 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
 constexpr int64_t kBwdDxWgs = 256;  // dx workgroups the fused token split aims at
 
 // whether dx and dc of this shape run in one launch (circ_bwd_kernel)
-template <int P>
+template <int P, bool WSPEC = false>
 bool bwd_fused_shape(int64_t k, int64_t q) {
   if constexpr (bwd_fusable<P>()) {
-    using S = TpShape<P, true>;
+    using S = TpShape<P, true, WSPEC>;
     return q <= S::CR && S::fits(static_cast<int>(q)) && S::lds_bytes(static_cast<int>(q)) <= kMaxLds &&
            k <= 0x7fffffff;
   } else {
@@ -282,13 +288,13 @@ bool bwd_fused_shape(int64_t k, int64_t q) {
   }
 }
 
-template <int P, class Io>
+template <int P, class Io, bool WSPEC = false>
 bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
                            int64_t k, int64_t q, bool acc, float* ws, hipStream_t s, int* status) {
   if constexpr (bwd_fusable<P>()) {
-    using S = TpShape<P, true>;
+    using S = TpShape<P, true, WSPEC>;
     using D = DtpShape<P>;
-    if (!bwd_fused_shape<P>(k, q)) return false;
+    if (!bwd_fused_shape<P, WSPEC>(k, q) || (WSPEC && ws)) return false;
     const DcSplit d = dc_split_tp<P>(batch, k, q, D::K.fwgs);
     if (!d.ok) return false;
     const int64_t gdy = d.gy, gdz = d.gz, tpw_dc = d.tpw, gdx = d.gx;
@@ -304,7 +310,7 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
     auto* pdx = static_cast<typename Io::T*>(dx);
     int st = RDFFT_OK;
     if (ws) {
-      hipLaunchKernelGGL((circ_bwd_kernel<P, Io, true>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
+      hipLaunchKernelGGL((circ_bwd_kernel<P, Io, true, WSPEC>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
                          static_cast<size_t>(lds), s, px, c, pdy, pdx, ws, batch, int(k), int(q), tpw_dc, int(gdx),
                          int(gdy), ndc, tpw_dx, int(gxx));
       st = launch_status();
@@ -312,7 +318,7 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
     } else {
       st = acc ? RDFFT_OK : launch_fill_zero(dc, q * k * P, s);  // dc is added into in the time domain
       if (st == RDFFT_OK) {
-        hipLaunchKernelGGL((circ_bwd_kernel<P, Io>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
+        hipLaunchKernelGGL((circ_bwd_kernel<P, Io, false, WSPEC>), dim3(static_cast<unsigned>(nwg)), dim3(S::K.nt),
                            static_cast<size_t>(lds), s, px, c, pdy, pdx, dc, batch, int(k), int(q), tpw_dc, int(gdx),
                            int(gdy), ndc, tpw_dx, int(gxx));
         st = launch_status();
@@ -327,14 +333,29 @@ bool launch_circ_bwd_fused(const void* x, const float* c, const void* dy, void* 
   }
 }
 
+// cs[row] = packed spectrum of c[row], rows = q k (weights given as spectra)
+template <int P>
+int launch_weight_spectra(const float* c, float* cs, int64_t rows, hipStream_t s) {
+  constexpr int CR = kSpecThreads / (P / elems_per_thread(P));
+  const int64_t groups = (rows + CR - 1) / CR;
+  const int64_t cap = static_cast<int64_t>(device_cus()) * 4;
+  const int64_t grid = groups < cap ? groups : cap;
+  if (grid <= 0) return RDFFT_OK;
+  hipLaunchKernelGGL((weight_spectra_kernel<P>), dim3(static_cast<unsigned>(grid)), dim3(kSpecThreads), 0, s, c, cs,
+                     rows);
+  return launch_status();
+}
+
 // forward; a non-null zero[q k P] (a gradient accumulator of c) is cleared by
 // the token-persistent kernel as a side job, or by a fill where another runs
-template <int P, class Io>
+template <int P, class Io, bool WSPEC = false>
 int circ_fwd_p(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, hipStream_t s,
-               float* zero) {
+               float* zero, float* wout = nullptr) {
   const int64_t k = d_in / P, q = d_out / P;
-  bool zeroed = false;
-  const int st = launch_circ_product<P, Io>(x, c, y, batch, k, q, false, s, zero, zero ? q * k * P : 0, &zeroed);
+  bool zeroed = false, wrote = false;
+  int st = launch_circ_product<P, Io, WSPEC>(x, c, y, batch, k, q, false, s, zero, zero ? q * k * P : 0, &zeroed,
+                                             wout, &wrote);
+  if (st == RDFFT_OK && wout && !wrote) st = launch_weight_spectra<P>(c, wout, q * k, s);
   if (st != RDFFT_OK || !zero || zeroed) return st;
   return launch_fill_zero(zero, q * k * P, s);
 }
@@ -357,18 +378,19 @@ int64_t dc_token_ranges(int64_t batch, int64_t k, int64_t q, bool with_dx) {
 
 // backward; acc: add the token sum into dc instead of overwriting it;
 // ws: deterministic dc (see launch_circ_dc), overwritten, never with acc
-template <int P, class Io>
+template <int P, class Io, bool WSPEC = false>
 int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
                int64_t d_out, bool acc, hipStream_t s, float* ws = nullptr) {
   const int64_t k = d_in / P, q = d_out / P;
   if (batch == 0) return (dc && !acc) ? launch_fill_zero(dc, q * k * P, s) : RDFFT_OK;
   int fused_status = RDFFT_OK;
-  if (dx && dc && launch_circ_bwd_fused<P, Io>(x, c, dy, dx, dc, batch, k, q, acc, ws, s, &fused_status))
+  if (dx && dc && launch_circ_bwd_fused<P, Io, WSPEC>(x, c, dy, dx, dc, batch, k, q, acc, ws, s, &fused_status))
     return fused_status;
   bool zeroed = false;  // dc cleared by the dx kernel
   if (dx) {
     float* zero = (acc || ws) ? nullptr : dc;
-    const int st = launch_circ_product<P, Io>(dy, c, dx, batch, q, k, true, s, zero, zero ? q * k * P : 0, &zeroed);
+    const int st =
+        launch_circ_product<P, Io, WSPEC>(dy, c, dx, batch, q, k, true, s, zero, zero ? q * k * P : 0, &zeroed);
     if (st != RDFFT_OK) return st;
   }
   if (dc) return launch_circ_dc_any<P, Io>(x, dy, dc, batch, k, q, s, zeroed, acc, ws);
@@ -392,18 +414,24 @@ int circ_bwd_p(const void* x, const float* c, const void* dy, void* dx, float* d
     default: return RDFFT_ERR_SIZE;  \
   }
 
-template <class Io>
+template <class Io, bool WSPEC = false>
 int circ_fwd_dispatch(const void* x, const float* c, void* y, int64_t batch, int64_t d_in, int64_t d_out, int64_t p,
-                      hipStream_t s, float* zero) {
-#define CALL(P) circ_fwd_p<P, Io>(x, c, y, batch, d_in, d_out, s, zero)
+                      hipStream_t s, float* zero, float* wout = nullptr) {
+#define CALL(P) circ_fwd_p<P, Io, WSPEC>(x, c, y, batch, d_in, d_out, s, zero, wout)
   RDFFT_P_SWITCH(p, CALL)
 #undef CALL
 }
 
-template <class Io>
+template <class Io, bool WSPEC = false>
 int circ_bwd_dispatch(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch, int64_t d_in,
                       int64_t d_out, int64_t p, bool acc, hipStream_t s, float* ws = nullptr) {
-#define CALL(P) circ_bwd_p<P, Io>(x, c, dy, dx, dc, batch, d_in, d_out, acc, s, ws)
+#define CALL(P) circ_bwd_p<P, Io, WSPEC>(x, c, dy, dx, dc, batch, d_in, d_out, acc, s, ws)
+  RDFFT_P_SWITCH(p, CALL)
+#undef CALL
+}
+
+inline int weight_spectra_dispatch(const float* c, float* cs, int64_t rows, int64_t p, hipStream_t s) {
+#define CALL(P) launch_weight_spectra<P>(c, cs, rows, s)
   RDFFT_P_SWITCH(p, CALL)
 #undef CALL
 }
@@ -626,6 +654,52 @@ int circulant_bwd_acc(const void* x, const float* c, const void* dy, void* dx, f
   hipStream_t s = static_cast<hipStream_t>(stream);
   return rdfft::by_dtype(dtype, [&](auto io) {
     return rdfft::circ_bwd_dispatch<decltype(io)>(x, c, dy, dx, dc, batch, d_in, d_out, p, true, s);
+  });
+}
+
+int circulant_weight_spectra(const float* c, float* cs, int64_t d_in, int64_t d_out, int64_t p, void* stream) {
+  const int st = rdfft::check_weight_spectra(c, cs, d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  return rdfft::weight_spectra_dispatch(c, cs, (d_out / p) * (d_in / p), p, static_cast<hipStream_t>(stream));
+}
+
+int circulant_fwd_step(const void* x, const float* c, void* y, float* dc, float* cs, int64_t batch, int64_t d_in,
+                       int64_t d_out, int64_t p, int dtype, void* stream) {
+  int st = dc ? rdfft::check_circulant_fwd_zero(x, c, y, dc, batch, d_in, d_out, p, dtype)
+              : rdfft::check_circulant_fwd(x, c, y, batch, d_in, d_out, p, dtype);
+  if (st == RDFFT_OK) st = rdfft::check_fwd_step_spectra(x, c, y, dc, cs, batch, d_in, d_out, p, dtype);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0) {
+    st = rdfft::weight_spectra_dispatch(c, cs, (d_out / p) * (d_in / p), p, s);
+    return (st == RDFFT_OK && dc) ? rdfft::launch_fill_zero(dc, (d_out / p) * d_in, s) : st;
+  }
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_fwd_dispatch<decltype(io)>(x, c, y, batch, d_in, d_out, p, s, dc, cs);
+  });
+}
+
+int circulant_fwd_spec(const void* x, const float* cs, void* y, float* dc, int64_t batch, int64_t d_in, int64_t d_out,
+                       int64_t p, int dtype, void* stream) {
+  int st = dc ? rdfft::check_circulant_fwd_zero(x, cs, y, dc, batch, d_in, d_out, p, dtype)
+              : rdfft::check_circulant_fwd(x, cs, y, batch, d_in, d_out, p, dtype);
+  if (st == RDFFT_OK) st = rdfft::check_spec_size(d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0) return dc ? rdfft::launch_fill_zero(dc, (d_out / p) * d_in, s) : RDFFT_OK;
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_fwd_dispatch<decltype(io), true>(x, cs, y, batch, d_in, d_out, p, s, dc);
+  });
+}
+
+int circulant_bwd_spec(const void* x, const float* cs, const void* dy, void* dx, float* dc, int accumulate,
+                       int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream) {
+  int st = rdfft::check_circulant_bwd(x, cs, dy, dx, dc, batch, d_in, d_out, p, dtype);
+  if (st == RDFFT_OK) st = rdfft::check_spec_size(d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return rdfft::by_dtype(dtype, [&](auto io) {
+    return rdfft::circ_bwd_dispatch<decltype(io), true>(x, cs, dy, dx, dc, batch, d_in, d_out, p, accumulate != 0, s);
   });
 }
 

@@ -139,4 +139,37 @@ inline int check_det_workspace(const void* x, const float* c, const void* dy, co
   return RDFFT_OK;
 }
 
+// weights given as packed spectra: the kernels read them through one buffer
+// resource with 32-bit byte offsets, so the q k p floats of cs, plus one row
+// of reads aimed past their end, stay below 2^31 bytes
+inline int check_spec_size(int64_t d_in, int64_t d_out, int64_t p) {
+  return (d_out / p) * d_in * 4 + 4 * p <= int64_t{0x7fffffff} ? RDFFT_OK : RDFFT_ERR_SIZE;
+}
+
+// circulant_weight_spectra: c and cs are separate [q, k, p] fp32 buffers
+inline int check_weight_spectra(const float* c, const float* cs, int64_t d_in, int64_t d_out, int64_t p) {
+  int st = check_circulant_dims(0, d_in, d_out, p);
+  if (st == RDFFT_OK) st = check_spec_size(d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  if (c == nullptr || cs == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(c) || !aligned16(cs)) return RDFFT_ERR_ALIGN;
+  const int64_t cb = (d_out / p) * d_in * 4;
+  return overlaps(cs, cb, c, cb) ? RDFFT_ERR_ALIAS : RDFFT_OK;
+}
+
+// circulant_fwd_step's output cs[q, k, p] (fp32): required, separate from
+// every other buffer of the call (the other arguments checked before)
+inline int check_fwd_step_spectra(const void* x, const float* c, const void* y, const float* dc, const float* cs,
+                                  int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype) {
+  const int st = check_spec_size(d_in, d_out, p);
+  if (st != RDFFT_OK) return st;
+  if (cs == nullptr || c == nullptr) return RDFFT_ERR_NULL;
+  if (!aligned16(cs)) return RDFFT_ERR_ALIGN;
+  const int64_t eb = dtype_bytes(dtype), cb = (d_out / p) * d_in * 4;
+  if (overlaps(cs, cb, c, cb) || overlaps(cs, cb, dc, cb) || overlaps(cs, cb, x, batch * d_in * eb) ||
+      overlaps(cs, cb, y, batch * d_out * eb))
+    return RDFFT_ERR_ALIAS;
+  return RDFFT_OK;
+}
+
 }  // namespace rdfft

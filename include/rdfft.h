@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RDFFT_ABI_VERSION 5
+#define RDFFT_ABI_VERSION 6
 
 /* storage types */
 #define RDFFT_F32 0
@@ -151,6 +151,62 @@ int circulant_fwd_zero(const void* x, const float* c, void* y, float* dc, int64_
  */
 int circulant_bwd_acc(const void* x, const float* c, const void* dy, void* dx, float* dc, int64_t batch,
                       int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
+
+/*
+ * The layer with its weights given as packed spectra (Paper-Notes page,
+ * "循环矩阵训练适配": the products above need FFT(c), never c itself).  A
+ * caller that keeps cs = FFT(c) in a buffer of c's size, computed once per
+ * value of c (once per optimizer step), saves the kernels from transforming
+ * weight rows at every call: they read the weights' bins from cs.  c itself
+ * is never overwritten (its spectra would not return it bitwise).
+ *
+ * circulant_weight_spectra -- cs[i, j, :] = packed FFT of c[i, j, :] (the
+ * layout at the top of this file), for every block of the layer.
+ *   c   [q, k, p]  float, read only
+ *   cs  [q, k, p]  float, written; must not overlap c
+ * p a power of two in [2, 4096]; d_in, d_out positive multiples of p with
+ * q k p floats at most 2^31 - 1 - 4p bytes (RDFFT_ERR_SIZE otherwise).
+ */
+int circulant_weight_spectra(const float* c, float* cs, int64_t d_in, int64_t d_out, int64_t p, void* stream);
+
+/*
+ * circulant_fwd_step -- the forward of a training step from c: circulant_fwd
+ * (circulant_fwd_zero when dc is not NULL) that also writes the weight
+ * spectra cs, as circulant_weight_spectra would, for circulant_bwd_spec.
+ * The forward transforms the weight rows anyway; where it runs its token-
+ * persistent kernel, that launch stores them, otherwise one more launch
+ * computes them.
+ *   cs  [q, k, p]  float, written; must not overlap x, c, y or dc
+ * Other arguments, checks and statuses as circulant_fwd and
+ * circulant_fwd_zero, plus the size limit of circulant_weight_spectra; cs is
+ * written when batch == 0 too.
+ */
+int circulant_fwd_step(const void* x, const float* c, void* y, float* dc, float* cs, int64_t batch, int64_t d_in,
+                       int64_t d_out, int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_fwd_spec -- circulant_fwd (or circulant_fwd_zero when dc is not
+ * NULL) from the weight spectra cs that circulant_weight_spectra wrote.
+ *   cs  [q, k, p]  float, read only, packed spectra of the weight rows
+ *   dc  [q, k, p]  float or NULL: when given, set to zero as by
+ *                  circulant_fwd_zero (also when batch == 0)
+ * Other arguments, checks and statuses as circulant_fwd and
+ * circulant_fwd_zero, with cs in the place of c, plus the size limit of
+ * circulant_weight_spectra.
+ */
+int circulant_fwd_spec(const void* x, const float* cs, void* y, float* dc, int64_t batch, int64_t d_in, int64_t d_out,
+                       int64_t p, int dtype, void* stream);
+
+/*
+ * circulant_bwd_spec -- circulant_bwd (accumulate == 0: dc overwritten) or
+ * circulant_bwd_acc (accumulate != 0: the token sum added into dc) from the
+ * weight spectra cs.  dx needs cs; dc is computed from x and dy alone, as in
+ * those calls, with the same order-of-summation caveat.  Arguments, checks
+ * and statuses as circulant_bwd, with cs in the place of c, plus the size
+ * limit of circulant_weight_spectra.
+ */
+int circulant_bwd_spec(const void* x, const float* cs, const void* dy, void* dx, float* dc, int accumulate,
+                       int64_t batch, int64_t d_in, int64_t d_out, int64_t p, int dtype, void* stream);
 
 /*
  * circulant_bwd_det_workspace -- bytes of the workspace circulant_bwd_det

@@ -172,6 +172,91 @@ def _det_workspace():
     return [(f, a, e) for a, e in cases]
 
 
+def _weight_spectra():
+    # c and cs are 4 x 4 x 16 fp32 (1 KiB); every valid call would launch, so
+    # only failing ones; 65536 x 65536 features at p = 2 make cs 8 GiB, past
+    # the 2 GiB of one buffer resource
+    f = "circulant_weight_spectra"
+    T = 1 << 40
+    cases = [
+        ((None, B_, 64, 64, 16), NULL),
+        ((C_, None, 64, 64, 16), NULL),
+        ((C_, B_, 64, 64, 12), SIZE),
+        ((C_, B_, 64, 64, 8192), SIZE),
+        ((C_, B_, 60, 64, 16), SHAPE),
+        ((C_, B_, 64, 0, 16), SHAPE),
+        ((C_, 0x200004, 64, 64, 16), ALIGN),
+        ((C_, 0x300000 + 512, 64, 64, 16), ALIAS),
+        ((T, 2 * T, 65536, 65536, 2), SIZE),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
+def _circ_fwd_spec():
+    # circulant_fwd's checks with cs for c, dc optional, and the size limit of
+    # the spectra; an empty batch without dc launches nothing
+    f = "circulant_fwd_spec"
+    T = 1 << 40
+    cases = [
+        ((A, C_, B_, None, 0, 64, 64, 16, F32), OK),
+        ((None, C_, B_, None, 2, 64, 64, 16, F32), NULL),
+        ((A, None, B_, DC, 2, 64, 64, 16, BF16), NULL),
+        ((A, C_, B_, None, 2, 64, 64, 12, F32), SIZE),
+        ((A, C_, B_, DC, 2, 64, 72, 16, F32), SHAPE),
+        ((A, C_, B_, None, 2, 64, 64, 16, 3), DTYPE),
+        ((A, C_, B_, 0x500008, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, 0x100000 + 64, None, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, 0x300000 + 256, 2, 64, 64, 16, F32), ALIAS),
+        ((T, 2 * T, 3 * T, None, 2, 65536, 65536, 2, F32), SIZE),
+        ((T, 2 * T, 3 * T, 4 * T, 2, 65536, 65536, 2, BF16), SIZE),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
+def _circ_fwd_step():
+    # circulant_fwd's checks, dc optional, cs required and separate from every
+    # other buffer; an empty batch still writes cs, so it would launch: not listed
+    f = "circulant_fwd_step"
+    CS, T = 0x600000, 1 << 40
+    cases = [
+        ((A, C_, B_, DC, None, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, None, None, 0, 64, 64, 16, F32), NULL),
+        ((A, None, B_, DC, CS, 0, 64, 64, 16, F32), NULL),
+        ((None, C_, B_, DC, CS, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DC, CS, 2, 64, 64, 12, F32), SIZE),
+        ((A, C_, B_, DC, CS, 2, 64, 48, 32, F32), SHAPE),
+        ((A, C_, B_, DC, CS, 2, 64, 64, 16, 6), DTYPE),
+        ((A, C_, B_, DC, 0x600004, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, DC, 0x300000 + 512, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, DC, 0x500000 + 512, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, None, 0x100000 + 64, 2, 64, 64, 16, BF16), ALIAS),
+        ((A, C_, B_, None, 0x200000 + 64, 2, 64, 64, 16, F32), ALIAS),
+        ((T, 2 * T, 3 * T, 4 * T, 5 * T, 2, 65536, 65536, 2, F32), SIZE),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
+def _circ_bwd_spec():
+    # circulant_bwd's checks with cs for c (the seventh argument is the
+    # accumulate flag) and the size limit of the spectra
+    f = "circulant_bwd_spec"
+    T = 1 << 40
+    cases = [
+        ((A, C_, B_, None, None, 0, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, 1, 0, 64, 64, 16, F32), OK),
+        ((A, C_, B_, DX, None, 0, 0, 64, 64, 16, F32), OK),
+        ((A, None, B_, DX, DC, 0, 2, 64, 64, 16, F32), NULL),
+        ((A, C_, B_, DX, DC, 1, 2, 64, 64, 5, F32), SIZE),
+        ((A, C_, B_, DX, DC, 0, 2, 48, 64, 32, F32), SHAPE),
+        ((A, C_, B_, DX, DC, 0, 2, 64, 64, 16, 9), DTYPE),
+        ((A, C_, B_, 0x400004, DC, 0, 2, 64, 64, 16, F32), ALIGN),
+        ((A, C_, B_, DX, 0x300000 + 16, 1, 2, 64, 64, 16, F32), ALIAS),
+        ((A, C_, B_, 0x200000 + 64, DC, 0, 2, 64, 64, 16, F32), ALIAS),
+        ((T, 2 * T, 3 * T, 4 * T, 5 * T, 1, 2, 65536, 65536, 2, F32), SIZE),
+    ]
+    return [(f, a, e) for a, e in cases]
+
+
 def _spectrum(fn):
     # argument order: (source, destination, ...): packed then spec for unpack, spec then packed for pack
     cases = [((A, B_, 0, 512, F32), OK), ((None, B_, 4, 512, F32), NULL), ((A, None, 4, 512, BF16), NULL)]
@@ -192,5 +277,6 @@ def _rdfft2d(fn):
 
 
 CASES = (_rdfft("rdfft_forward") + _rdfft("rdfft_inverse") + _circ_fwd() + _circ_bwd() + _circ_fwd_zero()
-         + _circ_bwd_acc() + _circ_bwd_det() + _circ_bwd_det_noalloc() + _det_workspace() + _spectrum("rdfft_unpack")
+         + _circ_bwd_acc() + _circ_bwd_det() + _circ_bwd_det_noalloc() + _det_workspace() + _weight_spectra()
+         + _circ_fwd_spec() + _circ_fwd_step() + _circ_bwd_spec() + _spectrum("rdfft_unpack")
          + _spectrum("rdfft_pack") + _rdfft2d("rdfft2d_forward") + _rdfft2d("rdfft2d_inverse"))

@@ -14,6 +14,13 @@
 //   run_abi circ_step  <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <y> <dx|-> <dc>
 //                      (circulant_fwd_zero into a dc that holds garbage, then
 //                      circulant_bwd_acc twice: dc = 2 x the gradient)
+//   run_abi circ_spec  <batch> <d_in> <d_out> <p> <dtype> <x> <c> <dy> <y> <y2> <dx|-> <dc> <cs>
+//                      (the weights given as spectra: circulant_fwd_step
+//                      writing y and cs and clearing a dc that holds garbage;
+//                      circulant_weight_spectra into a second buffer, which
+//                      must equal cs bitwise; circulant_fwd_spec from it into
+//                      y2; then circulant_bwd_spec overwriting dc and once
+//                      more adding into it: dc = 2 x the gradient)
 //   run_abi cases      (stdin: one call per line, "<entry point> <arg> ...", a
 //                      pointer argument as an integer address or "null"; prints
 //                      each call's status, one per line)
@@ -124,6 +131,18 @@ int call_case(const std::string& line) {
   if (f == "circulant_bwd_det_workspace" && n == 6)
     return circulant_bwd_det_workspace(num(1), num(2), num(3), num(4), int(num(5)),
                                        static_cast<int64_t*>(ptr(6)));
+  if (f == "circulant_weight_spectra" && n == 5)
+    return circulant_weight_spectra(static_cast<const float*>(ptr(1)), static_cast<float*>(ptr(2)), num(3), num(4),
+                                    num(5), nullptr);
+  if (f == "circulant_fwd_step" && n == 10)
+    return circulant_fwd_step(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), static_cast<float*>(ptr(4)),
+                              static_cast<float*>(ptr(5)), num(6), num(7), num(8), num(9), int(num(10)), nullptr);
+  if (f == "circulant_fwd_spec" && n == 9)
+    return circulant_fwd_spec(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), static_cast<float*>(ptr(4)), num(5),
+                              num(6), num(7), num(8), int(num(9)), nullptr);
+  if (f == "circulant_bwd_spec" && n == 11)
+    return circulant_bwd_spec(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
+                              int(num(6)), num(7), num(8), num(9), num(10), int(num(11)), nullptr);
   if (f == "circulant_bwd" && n == 10)
     return circulant_bwd(ptr(1), static_cast<const float*>(ptr(2)), ptr(3), ptr(4), static_cast<float*>(ptr(5)),
                          num(6), num(7), num(8), num(9), int(num(10)), nullptr);
@@ -225,6 +244,37 @@ int main(int argc, char** argv) {
     write_file(argv[10], y);
     if (want_dx) write_file(argv[11], dx);
     write_file(argv[12], dc);
+  } else if (op == "circ_spec" && argc == 15) {
+    const int64_t b = arg(argv, 2), di = arg(argv, 3), dout = arg(argv, 4), p = arg(argv, 5);
+    const int dt = static_cast<int>(arg(argv, 6));
+    Buf x = read_file(argv[7], b * di * esize(dt));
+    Buf c = read_file(argv[8], (dout / p) * di * 4);
+    Buf dy = read_file(argv[9], b * dout * esize(dt));
+    const bool want_dx = std::strcmp(argv[12], "-") != 0;
+    Buf cs = alloc((dout / p) * di * 4), cs2 = alloc((dout / p) * di * 4);
+    Buf y = alloc(b * dout * esize(dt)), y2 = alloc(b * dout * esize(dt));
+    Buf dx = alloc(b * di * esize(dt));
+    Buf dc = alloc((dout / p) * di * 4);
+    for (size_t i = 0; i < cs.n / 4; ++i) static_cast<float*>(cs.p)[i] = static_cast<float*>(cs2.p)[i] = -555.0f;
+    for (size_t i = 0; i < dc.n / 4; ++i) static_cast<float*>(dc.p)[i] = 12345.0f;  // cleared by the forward
+    auto* pcs = static_cast<float*>(cs.p);
+    st = circulant_fwd_step(x.p, static_cast<const float*>(c.p), y.p, static_cast<float*>(dc.p), pcs, b, di, dout, p, dt,
+                            nullptr);
+    if (st == RDFFT_OK)
+      st = circulant_weight_spectra(static_cast<const float*>(c.p), static_cast<float*>(cs2.p), di, dout, p, nullptr);
+    if (st == RDFFT_OK && std::memcmp(cs.p, cs2.p, cs.n) != 0) {
+      std::fprintf(stderr, "circulant_fwd_step and circulant_weight_spectra wrote different spectra\n");
+      return 3;
+    }
+    if (st == RDFFT_OK) st = circulant_fwd_spec(x.p, pcs, y2.p, nullptr, b, di, dout, p, dt, nullptr);
+    for (int rep = 0; rep < 2 && st == RDFFT_OK; ++rep)
+      st = circulant_bwd_spec(x.p, pcs, dy.p, want_dx ? dx.p : nullptr, static_cast<float*>(dc.p), rep, b, di, dout, p,
+                              dt, nullptr);
+    write_file(argv[10], y);
+    write_file(argv[11], y2);
+    if (want_dx) write_file(argv[12], dx);
+    write_file(argv[13], dc);
+    write_file(argv[14], cs);
   } else if (op == "cases" && argc == 2) {
     char buf[4096];
     while (std::fgets(buf, sizeof(buf), stdin)) {

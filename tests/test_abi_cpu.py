@@ -42,6 +42,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"rdfft_abi_version", "rdfft_status_string", "rdfft_forward", "rdfft_inverse",
                           "circulant_fwd", "circulant_bwd", "circulant_fwd_zero", "circulant_bwd_acc",
                           "circulant_bwd_det", "circulant_bwd_det_workspace", "circulant_bwd_det_noalloc",
+                          "circulant_weight_spectra", "circulant_fwd_step", "circulant_fwd_spec", "circulant_bwd_spec",
                           "rdfft_unpack", "rdfft_pack",
                           "rdfft2d_forward", "rdfft2d_inverse"}
     for n in names:
@@ -77,7 +78,8 @@ def test_validation(L, fn, args, want):
     # its last one); circulant_bwd_det's seventh is the workspace size
     n_ptr = {"rdfft_forward": 1, "rdfft_inverse": 1, "circulant_fwd": 3, "circulant_bwd": 5,
              "circulant_fwd_zero": 4, "circulant_bwd_acc": 5, "circulant_bwd_det": 6,
-             "circulant_bwd_det_workspace": 0, "circulant_bwd_det_noalloc": 5, "rdfft_unpack": 2,
+             "circulant_bwd_det_workspace": 0, "circulant_bwd_det_noalloc": 5, "circulant_weight_spectra": 2,
+             "circulant_fwd_spec": 4, "circulant_fwd_step": 5, "circulant_bwd_spec": 5, "rdfft_unpack": 2,
              "rdfft_pack": 2, "rdfft2d_forward": 1, "rdfft2d_inverse": 1}[fn]
     ptrs = set(range(n_ptr)) | ({len(args) - 1} if fn == "circulant_bwd_det_workspace" else set())
     cargs = [(ctypes.c_void_p(a) if a is not None else None) if i in ptrs else a for i, a in enumerate(args)]

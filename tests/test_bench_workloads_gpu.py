@@ -10,7 +10,10 @@ device's input values:
   rotation of 32 training steps; steps 0 and 31 in full (y and dx per token
   row, dc of step 31, which the rotation leaves in the buffer);
 - the 128 adapters (4096x4096, p=1024, 2048 tokens): one replayed step;
-  adapters 0, 64 and 127 in full.
+  adapters 0, 64 and 127 in full;
+each in both forms bench.py times: the weights transformed at every call, and
+their spectra kept from forward to backward (circulant_fwd_step and
+circulant_bwd_spec).
 
 Every step of the rotation and every adapter is also checked through the
 adjoint identities <dy, y> = <dx, x> (= <dc, c> where dc is at hand), which
@@ -57,10 +60,11 @@ def _oracle_check(x, c, dy, y, dx, dc=None):
         assert row_relerr(to_f64(dc).reshape(-1, p), dco.reshape(-1, p)) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("spectra", [False, True])
 @pytest.mark.parametrize("p", [128, 512, 4096])
-def test_single_layer_rotation(p):
-    print(f"bench single layer D=4096 B=256 p={p}: one replayed rotation", flush=True)
-    w = bench.circ_layer_setup(256, 4096, p)
+def test_single_layer_rotation(p, spectra):
+    print(f"bench single layer D=4096 B=256 p={p} spectra={spectra}: one replayed rotation", flush=True)
+    w = bench.circ_layer_setup(256, 4096, p, spectra=spectra)
     g = bench._graph(w["rot"])
     for t in w["ys"] + w["dxs"] + [w["dc"]]:
         t.fill_(float("nan"))
@@ -76,9 +80,10 @@ def test_single_layer_rotation(p):
     _oracle_check(w["xs"][-1], w["c"], w["dys"][-1], w["ys"][-1], w["dxs"][-1], w["dc"])
 
 
-def test_adapters_step():
-    print("bench 128 adapters 4096x4096 p=1024, 2048 tokens: one replayed step", flush=True)
-    w = bench.circ_adapters_setup()
+@pytest.mark.parametrize("spectra", [False, True])
+def test_adapters_step(spectra):
+    print(f"bench 128 adapters 4096x4096 p=1024, 2048 tokens spectra={spectra}: one replayed step", flush=True)
+    w = bench.circ_adapters_setup(spectra=spectra)
     g = bench._graph(w["step"])
     for t in w["ys"] + w["dxs"] + w["dcs"]:
         t.fill_(float("nan"))

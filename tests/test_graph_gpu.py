@@ -99,6 +99,40 @@ def test_training_step_graph_replays(b, d, p, want_dx):
         assert err <= 1e-5, (i, err)
 
 
+# the training step with the weights as spectra: circulant_fwd_step writes cs
+# (in its launch at p = 128 and 4096, with a launch of its own at p = 16) and
+# clears dc; circulant_bwd_spec reads cs and adds into dc
+@pytest.mark.parametrize("b,d,p,want_dx", [(64, 1024, 128, True), (32, 4096, 4096, True), (24, 256, 16, True),
+                                           (40, 512, 64, False)])
+def test_spectral_step_graph_replays(b, d, p, want_dx):
+    x, _ = device_input((b, d), syn.WL_TEST, syn.T_X, 36, dtype="bf16")
+    c, _ = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 36, scale=1 / 32)
+    dy, _ = device_input((b, d), syn.WL_TEST, syn.T_DY, 36, dtype="bf16")
+    cs0 = bcl.circulant_weight_spectra(c)
+    y0 = bcl.circulant_fwd(x, c)  # circulant_fwd_step's y is circulant_fwd's
+    dx0, dc0 = bcl.circulant_bwd_spec(x, cs0, dy, need_dx=want_dx)
+    y, dc, cs = torch.empty_like(y0), torch.empty_like(dc0), torch.empty_like(cs0)
+    dx = torch.empty_like(x) if want_dx else None
+
+    def step():
+        bcl.circulant_fwd_step(x, c, cs, y, dc=dc)
+        bcl.circulant_bwd_spec(x, cs, dy, dx=dx, dc=dc, need_dx=want_dx, accumulate=True)
+
+    g = _capture(step)
+    for i in range(4):
+        for t in (y, dx, dc, cs):
+            if t is not None:
+                t.fill_(float("nan"))  # eager work; the replay must clear or overwrite everything
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cs, cs0) and torch.equal(y, y0), i
+        if want_dx:
+            assert torch.equal(dx, dx0), i
+        err = float((dc - dc0).norm() / dc0.norm())
+        assert err <= 1e-5, (i, err)
+
+
 @pytest.mark.parametrize("b,d,p,want_dx", [(64, 1024, 128, True), (24, 256, 16, True), (40, 512, 64, False)])
 def test_deterministic_dc_graph_replays(b, d, p, want_dx):
     # circulant_bwd_det captured: every replay gives the eager result bit for bit

@@ -93,7 +93,7 @@ def test_transform_calls(exe, tmp_path, rows, p, dt):
     assert _relerr(_read(f, (rows, p), dt), ro.rdfft_forward(xr)) <= {"f32": 1e-5, "bf16": 2e-2, "f16": 1e-3}[dt]
 
 
-@pytest.mark.parametrize("batch,d_in,d_out,p", [(5, 64, 48, 16), (3, 512, 1024, 256)])
+@pytest.mark.parametrize("batch,d_in,d_out,p", [(5, 64, 48, 16), (3, 512, 1024, 256), (4, 640, 384, 128)])
 def test_circulant_calls(exe, tmp_path, batch, d_in, d_out, p):
     q, k = d_out // p, d_in // p
     xt, xr = syn.cast_like_device(syn.normal((batch, d_in), syn.WL_TEST, syn.T_X, 60 + p), "f32")
@@ -124,5 +124,16 @@ def test_circulant_calls(exe, tmp_path, batch, d_in, d_out, p):
                        timeout=300)
     _check_clean(r)
     assert _relerr(_read(fy, (batch, d_out), "f32"), co.circulant_forward_dense(xr, cr)) <= 1e-5
+    assert _relerr(_read(fdx, (batch, d_in), "f32"), dxo) <= 1e-5
+    assert _relerr(_read(fdc, (q * k, p), "f32"), 2 * dco.reshape(q * k, p)) <= 1e-5
+    # the weights given as spectra: circulant_fwd_step, circulant_weight_spectra,
+    # circulant_fwd_spec and circulant_bwd_spec
+    fy2, fcs = str(tmp_path / "y2"), str(tmp_path / "cs")
+    r = subprocess.run([exe, "circ_spec", *dims, fx, fc, fg, fy, fy2, fdx, fdc, fcs], capture_output=True, text=True,
+                       env=ENV, timeout=300)
+    _check_clean(r)
+    assert _relerr(_read(fcs, (q * k, p), "f32"), ro.rdfft_forward(cr.reshape(q * k, p))) <= 1e-5
+    assert _relerr(_read(fy, (batch, d_out), "f32"), co.circulant_forward_dense(xr, cr)) <= 1e-5
+    assert _relerr(_read(fy2, (batch, d_out), "f32"), co.circulant_forward_dense(xr, cr)) <= 1e-5
     assert _relerr(_read(fdx, (batch, d_in), "f32"), dxo) <= 1e-5
     assert _relerr(_read(fdc, (q * k, p), "f32"), 2 * dco.reshape(q * k, p)) <= 1e-5

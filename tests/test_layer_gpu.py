@@ -17,14 +17,15 @@ from tests.gpu_util import TOL, TORCH_DT, device_input, row_relerr, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _layer_with(c: torch.Tensor) -> bcl.BlockCirculantLinear:
+def _layer_with(c: torch.Tensor, weight_spectra: bool = False) -> bcl.BlockCirculantLinear:
     q, k, p = c.shape
-    layer = bcl.BlockCirculantLinear(k * p, q * p, p, device="cuda:0")
+    layer = bcl.BlockCirculantLinear(k * p, q * p, p, device="cuda:0", weight_spectra=weight_spectra)
     with torch.no_grad():
         layer.c.copy_(c)
     return layer
 
 
+@pytest.mark.parametrize("weight_spectra", [False, True])
 @pytest.mark.parametrize("batch,d_in,d_out,p,dtype,dense", [
     (3, 64, 64, 16, "f32", True),
     (5, 96, 160, 32, "bf16", True),
@@ -32,13 +33,13 @@ def _layer_with(c: torch.Tensor) -> bcl.BlockCirculantLinear:
     (4, 2048, 4096, 1024, "bf16", False),
     (6, 512, 256, 64, "f16", True),
 ])
-def test_autograd_matches_oracle(batch, d_in, d_out, p, dtype, dense):
+def test_autograd_matches_oracle(batch, d_in, d_out, p, dtype, dense, weight_spectra):
     q, k = d_out // p, d_in // p
-    print(f"layer autograd B={batch} d_in={d_in} d_out={d_out} p={p} {dtype}", flush=True)
+    print(f"layer autograd B={batch} d_in={d_in} d_out={d_out} p={p} {dtype} spectra={weight_spectra}", flush=True)
     x, xr = device_input((batch, d_in), syn.WL_TEST, syn.T_X, 11, dtype=dtype)
     c, cr = device_input((q, k, p), syn.WL_TEST, syn.T_C, 11, scale=1 / d_in**0.5)
     dy, dyr = device_input((batch, d_out), syn.WL_TEST, syn.T_DY, 11, dtype=dtype)
-    layer = _layer_with(c)
+    layer = _layer_with(c, weight_spectra)
     x.requires_grad_(True)
     y = layer(x)
     y.backward(dy)
@@ -94,6 +95,39 @@ def test_second_backward_and_no_grad():
     assert torch.equal(y2, y.detach())
 
 
+def test_weight_spectra_steps_and_kept_spectra():
+    # with weight_spectra: a frozen c (dx only) through circulant_fwd_step /
+    # circulant_bwd_spec, two training steps adding into .grad, and forwards
+    # without grad that reuse the kept spectra until c changes
+    x, xr = device_input((6, 512), syn.WL_TEST, syn.T_X, 15, dtype="bf16")
+    c, cr = device_input((4, 4, 128), syn.WL_TEST, syn.T_C, 15, scale=1 / 512**0.5)
+    dy, dyr = device_input((6, 512), syn.WL_TEST, syn.T_DY, 15, dtype="bf16")
+    layer = _layer_with(c, weight_spectra=True)
+    layer(x).backward(dy)
+    layer(x).backward(dy)
+    torch.cuda.synchronize()
+    _, dco = co.circulant_backward_fft(xr, cr, dyr)
+    assert row_relerr(to_f64(layer.c.grad).reshape(-1, 128), 2 * dco.reshape(-1, 128)) <= TOL["f32"]
+    layer.c.requires_grad_(False)
+    xg = x.detach().clone().requires_grad_(True)
+    layer(xg).backward(dy)
+    dxo, _ = co.circulant_backward_fft(xr, cr, dyr)
+    torch.cuda.synchronize()
+    assert row_relerr(to_f64(xg.grad), dxo) <= TOL["bf16"]
+    with torch.no_grad():
+        y1 = layer(x)
+        cs1 = layer._cs
+        y2 = layer(x)
+        assert layer._cs is cs1  # kept
+        layer.c.mul_(2.0)  # c changes: the spectra are computed again
+        y3 = layer(x)
+        assert layer._cs is not cs1
+    torch.cuda.synchronize()
+    yo = co.circulant_forward_fft(xr, cr)
+    assert torch.equal(y1, y2)
+    assert row_relerr(to_f64(y1), yo) <= TOL["bf16"] and row_relerr(to_f64(y3), 2 * yo) <= TOL["bf16"]
+
+
 def test_token_axes_and_transposed_input():
     # activations shaped (sequences, tokens, features), the leading axes being
     # tokens alike, and a non-contiguous input (the layer makes it contiguous)
@@ -121,16 +155,18 @@ def _nbytes(t: torch.Tensor) -> int:
     return -(-t.numel() * t.element_size() // 512) * 512
 
 
+@pytest.mark.parametrize("weight_spectra", [False, True])
 @pytest.mark.parametrize("batch,d,p,dtype", [(256, 4096, 128, "bf16"), (256, 4096, 512, "bf16"),
                                              (256, 4096, 4096, "bf16"), (2048, 4096, 1024, "bf16"),
                                              (1, 4096, 128, "f32")])
-def test_zero_workspace(batch, d, p, dtype):
-    """Peak allocation of forward + backward = y + dx + dc exactly."""
-    print(f"layer workspace B={batch} D={d} p={p} {dtype}", flush=True)
+def test_zero_workspace(batch, d, p, dtype, weight_spectra):
+    """Peak allocation of forward + backward = y + dx + dc exactly (+ the
+    weight spectra, the size of c, with weight_spectra)."""
+    print(f"layer workspace B={batch} D={d} p={p} {dtype} spectra={weight_spectra}", flush=True)
     x, _ = device_input((batch, d), syn.WL_TEST, syn.T_X, 13, dtype=dtype)
     c, _ = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 13, scale=1 / d**0.5)
     dy, _ = device_input((batch, d), syn.WL_TEST, syn.T_DY, 13, dtype=dtype)
-    layer = _layer_with(c)
+    layer = _layer_with(c, weight_spectra)
     x.requires_grad_(True)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -139,4 +175,5 @@ def test_zero_workspace(batch, d, p, dtype):
     y.backward(dy)
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated() - before
-    assert peak == _nbytes(y) + _nbytes(x.grad) + _nbytes(layer.c.grad), peak
+    spectra = _nbytes(layer.c) if weight_spectra else 0
+    assert peak == _nbytes(y) + _nbytes(x.grad) + _nbytes(layer.c.grad) + spectra, peak

@@ -165,6 +165,44 @@ def test_circulant_step(exe, tmp_path, batch, d_in, d_out, p, dt, want_dx):
     assert _relerr(_read(fdc, (q * k, p), "f32"), 2 * dco.reshape(q * k, p)) <= TOL["f32"]
 
 
+# the weights given as spectra: circulant_fwd_step (y, cs, and a dc that held
+# garbage cleared), circulant_weight_spectra (bitwise the cs of the forward,
+# checked by the driver), circulant_fwd_spec from cs, circulant_bwd_spec
+# overwriting dc, then adding into it (dc = 2 x the gradient).  Routes: the small-p kernels (p < 64
+# and p = 128 with 40 input blocks, more than one transform round holds), the
+# token-persistent tiles and the one-launch backward at every p from 64 to
+# 4096, output tiles past the last block (q = 3 and k = 5 at p = 128), and dc
+# without dx.
+SPEC_CASES = [(5, 64, 48, 16, "f32", True), (4, 96, 64, 32, "f32", False), (7, 256, 192, 64, "bf16", True),
+              (9, 640, 384, 128, "bf16", True), (9, 640, 384, 128, "bf16", False), (3, 5120, 384, 128, "f32", True),
+              (5, 512, 1024, 256, "f32", True), (6, 1024, 1536, 512, "bf16", True), (5, 2048, 4096, 1024, "bf16", True),
+              (3, 4096, 2048, 2048, "f32", True), (5, 4096, 4096, 4096, "bf16", True),
+              (2, 8192, 4096, 4096, "f16", False)]
+
+
+@pytest.mark.parametrize("batch,d_in,d_out,p,dt,want_dx", SPEC_CASES)
+def test_circulant_spec(exe, tmp_path, batch, d_in, d_out, p, dt, want_dx):
+    q, k = d_out // p, d_in // p
+    xt, xr = syn.cast_like_device(syn.normal((batch, d_in), syn.WL_TEST, syn.T_X, 990 + p), dt)
+    ct, cr = syn.cast_like_device(syn.normal((q, k, p), syn.WL_TEST, syn.T_C, 990 + p, d_in**-0.5), "f32")
+    gt, gr = syn.cast_like_device(syn.normal((batch, d_out), syn.WL_TEST, syn.T_DY, 990 + p), dt)
+    fx, fc, fg = str(tmp_path / "x"), str(tmp_path / "c"), str(tmp_path / "dy")
+    fy, fdx, fdc = str(tmp_path / "y"), str(tmp_path / "dx"), str(tmp_path / "dc")
+    fy2, fcs = str(tmp_path / "y2"), str(tmp_path / "cs")
+    _write(fx, xt)
+    _write(fc, ct)
+    _write(fg, gt)
+    _run(exe, "circ_spec", batch, d_in, d_out, p, DT[dt], fx, fc, fg, fy, fy2, fdx if want_dx else "-", fdc, fcs)
+    assert _relerr(_read(fcs, (q * k, p), "f32"), ro.rdfft_forward(cr.reshape(q * k, p))) <= TOL["f32"]
+    yo = co.circulant_forward_fft(xr, cr)
+    assert _relerr(_read(fy, (batch, d_out), dt), yo) <= TOL[dt]
+    assert _relerr(_read(fy2, (batch, d_out), dt), yo) <= TOL[dt]
+    dxo, dco = co.circulant_backward_fft(xr, cr, gr)
+    if want_dx:
+        assert _relerr(_read(fdx, (batch, d_in), dt), dxo) <= TOL[dt]
+    assert _relerr(_read(fdc, (q * k, p), "f32"), 2 * dco.reshape(q * k, p)) <= TOL["f32"]
+
+
 # the deterministic dc (workspace slices summed in order) on every route:
 # small-p kernels, token-persistent dc alone with packed-spectra slices (p = 64,
 # 128) and time-domain slices (p = 256), and the one-launch backward with dx

@@ -684,8 +684,10 @@ def bench_circ_forward_fixed(batch, d, p, spectra, steps=256, warmup=32, nrot=32
 
 def profile_circulant(reps=3):
     """Eager launches of the four circulant workloads (the zeroing forward, then
-    the accumulating backward with dx and dc, as the timed steps run them), for
-    counter collection under a profiler: no graphs, no timing."""
+    the accumulating backward with dx and dc, as the timed steps run them; then
+    the same from the weight spectra: the forward with fixed weights and the
+    accumulating backward), for counter collection under a profiler: no
+    graphs, no timing."""
     for name, (batch, d, p) in {"adapter": (2048, 4096, 1024), "p128": (256, 4096, 128), "p512": (256, 4096, 512),
                                 "p4096": (256, 4096, 4096)}.items():
         q = k = d // p
@@ -696,8 +698,13 @@ def profile_circulant(reps=3):
         for _ in range(reps):
             bcl.circulant_fwd_zero(x, c, dc)
             bcl.circulant_bwd_acc(x, c, dy, dc)
+        cs = bcl.circulant_weight_spectra(c)
+        for _ in range(reps):
+            bcl.circulant_fwd_spec(x, cs)
+            bcl.circulant_bwd_spec(x, cs, dy, dc=dc, accumulate=True)
         torch.cuda.synchronize()
-        log(f"profiled circulant {name}: B={batch} D={d} p={p}, {reps} x (forward, backward)")
+        log(f"profiled circulant {name}: B={batch} D={d} p={p}, {reps} x (forward, backward) from c and from its "
+            "spectra")
 
 
 def profile_2d(reps=3):
@@ -748,14 +755,22 @@ def trace_summary(trace_dir: str, steps: int, warmup: int, command: str) -> str:
     for r in rows:
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    head = [r for r in csv.DictReader(open(trace[0])) if "rdfft_fwd_kernel<512, rdfft::F32Io>" in r["Kernel_Name"]]
-    head.sort(key=lambda r: int(r["Start_Timestamp"]))
+    every = sorted(csv.DictReader(open(trace[0])), key=lambda r: int(r["Start_Timestamp"]))
+    head = [i for i, r in enumerate(every) if "rdfft_fwd_kernel<512, rdfft::F32Io>" in r["Kernel_Name"]]
     timed = head[warmup: warmup + steps]
     if timed:
-        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        d = [(int(every[i]["End_Timestamp"]) - int(every[i]["Start_Timestamp"])) / 1e3 for i in timed]
+        # idle time before each timed launch: from the end of the dispatch before it
+        idle = [(int(every[i]["Start_Timestamp"]) - int(every[i - 1]["End_Timestamp"])) / 1e3 for i in timed if i > 0]
         lines += ["", "Headline forward kernel, the timed region's dispatches only:", "",
-                  "| kernel | timed dispatches | avg us | min us | max us |", "|---|---|---|---|---|",
-                  f"| rdfft_fwd_kernel<512, F32Io> | {len(d)} | {np.mean(d):.2f} | {min(d):.2f} | {max(d):.2f} |"]
+                  "| kernel | timed dispatches | avg us | min us | max us | median idle before a launch, us |",
+                  "|---|---|---|---|---|---|",
+                  f"| rdfft_fwd_kernel<512, F32Io> | {len(d)} | {np.mean(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
+                  f"{float(np.median(idle)) if idle else 0.0:.1f} |",
+                  "",
+                  "bench.py queues the timed launches behind a spin kernel, so they run back to back (idle near 0).",
+                  "Where the tracer's handling of each dispatch leaves the GPU idle between them, the launches",
+                  "start on an idle GPU and take longer than in the untimed run."]
     return "\n".join(lines) + "\n"
 
 
@@ -849,18 +864,20 @@ def counter_summary(root: str):
             raise SystemExit("the circulant counter runs carry no calibration copy (take them with --calib-copy)")
         ff, wf = CALIB_KIB / fcal, CALIB_KIB / wcal
         kib = lambda b: b / 1024  # noqa: E731
-        work = [  # (kernel, workload, algorithmic reads KiB, algorithmic writes KiB)
-            ("circ_tp_kernel<1024, false, rdfft::Bf16Io>", "adapter forward", kib(2048 * 4096 * 2 + 16 * 1024 * 4),
-             kib(2048 * 4096 * 2 + 16 * 1024 * 4)),
-            ("circ_bwd_kernel<1024, rdfft::Bf16Io>", "adapter backward (dx and dc)",
-             kib(2 * 2048 * 4096 * 2 + 16 * 1024 * 4), kib(2048 * 4096 * 2 + 16 * 1024 * 4)),
-        ]
-        for pp in (128, 512, 4096):
-            cb = 4096 * 4096 // pp * 4
-            work.append((f"circ_tp_kernel<{pp}, false, rdfft::Bf16Io>", f"D=4096 B=256 p={pp} forward",
-                         kib(256 * 4096 * 2 + cb), kib(256 * 4096 * 2 + cb)))
-            work.append((f"circ_bwd_kernel<{pp}, rdfft::Bf16Io>", f"p={pp} backward (dx and dc)",
-                         kib(2 * 256 * 4096 * 2 + cb), kib(256 * 4096 * 2 + cb)))
+        work = []  # (kernel, workload, algorithmic reads KiB, algorithmic writes KiB)
+        for name, batch, pp in (("adapter", 2048, 1024), ("D=4096 B=256 p=128", 256, 128),
+                                ("D=4096 B=256 p=512", 256, 512), ("D=4096 B=256 p=4096", 256, 4096)):
+            act, cb = batch * 4096 * 2, 4096 * 4096 // pp * 4
+            work += [
+                (f"circ_tp_kernel<{pp}, false, rdfft::Bf16Io, false>", f"{name} forward", kib(act + cb),
+                 kib(act + cb)),
+                (f"circ_bwd_kernel<{pp}, rdfft::Bf16Io, false, false>", f"{name} backward (dx and dc)",
+                 kib(2 * act + cb), kib(act + cb)),
+                (f"circ_tp_kernel<{pp}, false, rdfft::Bf16Io, true>", f"{name} forward from the weight spectra",
+                 kib(act + cb), kib(act)),
+                (f"circ_bwd_kernel<{pp}, rdfft::Bf16Io, false, true>",
+                 f"{name} backward from the weight spectra (dx and dc)", kib(2 * act + cb), kib(act + cb)),
+            ]
         lines = []
         for kname, wl, ar, aw in work:
             key = next((k for k in f if kname in k), None)
@@ -884,8 +901,9 @@ def counter_summary(root: str):
             "```",
             "",
             f"Means over the dispatches of each kernel, KiB, scaled by the known-size copy (FETCH x {ff:.4f}, "
-            f"WRITE x {wf:.4f}).  Algorithmic: activations once, `c` once, `dc` once (fp32); the forward "
-            "also writes the zeros of `dc`, which the backward then adds into.",
+            f"WRITE x {wf:.4f}).  Algorithmic: activations once, `c` (or its spectra) once, `dc` once (fp32); "
+            "the forward from `c` also writes the zeros of `dc`, which the backward then adds into; the "
+            "forward from the spectra writes `y` alone.",
             "",
             "| kernel | workload | dispatches | algorithmic reads | measured reads | ratio | algorithmic writes | "
             "measured writes | ratio |",
@@ -960,8 +978,9 @@ def sq_summary(root: str, trace_dir: str) -> str:
         "set 2: `SQ_INSTS_SALU SQ_ACTIVE_INST_LDS SQ_INST_CYCLES_VMEM SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT "
         "SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE`.",
         "`--profile-circulant` launches each circulant workload three times eagerly (forward, then backward with",
-        "dx and dc): one adapter of the 128-adapter workload (4096x4096, p=1024, 2048 tokens) and the single",
-        "layer D=4096, B=256 at p = 128, 512, 4096, all bf16.  `--profile-2d` runs the 2D forward and inverse of",
+        "dx and dc), from `c` and from its spectra (kernels instantiated with `true` last): one adapter of the",
+        "128-adapter workload (4096x4096, p=1024, 2048 tokens) and the single layer D=4096, B=256 at",
+        "p = 128, 512, 4096, all bf16.  `--profile-2d` runs the 2D forward and inverse of",
         "one 4096x4096 fp32 array three times.  Means over the dispatches of each kernel.",
         "",
         "*VALU issue time* = VALU wave-instructions x 4 cycles / (1024 SIMDs x 2.4 GHz): the time the",

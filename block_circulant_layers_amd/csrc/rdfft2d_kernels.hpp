@@ -19,9 +19,15 @@ namespace rdfft {
 
 // Column pass.  A workgroup loads a tile of CL adjacent columns x all H rows
 // into LDS (row runs of CL elements, coalesced), transforms the columns CP at
-// a time (T = H/E threads per column, CP * T <= 1024 threads), and stores the
-// tile back the same way.  CL is the widest power of two whose tile fits the
-// LDS budget (64-byte runs from H = 2048 down, 32-byte runs at H = 4096).
+// a time (T = H/E threads per column, CP * T threads), and stores the tile
+// back the same way.  CL is the widest power of two whose tile fits the LDS
+// budget.  From H = 512 to 2048 the budget is 72 KB and the workgroup 512
+// threads, so that two workgroups share a CU and one's loads overlap the
+// other's transforms: fp32 forward / inverse, us, 144 KB and 1024 threads ->
+// 72 KB and 512 threads: 512x2048 34.4 / 29.4 -> 31.6 / 26.6, 1024x1024
+// 35.5 / 30.4 -> 31.9 / 27.2, 2048x2048 49.3 / 46.4 -> 46.3 / 43.2.  At
+// H = 256 (23.8 / 21.9 -> 30.9 / 26.6) and H = 4096 (4096x4096: 114.5 / 100.5
+// -> 123.6 / 102.3) the larger tile stays.
 // LDS stride of a tile column.  In the load and store loops a 32-lane half
 // wavefront covers 32/CL rows of the CL columns (CL < 32), or 32 columns of
 // one row: the column stride must be 32/CL modulo the 32 banks in the first
@@ -36,10 +42,11 @@ template <int H>
 struct ColShape {
   static constexpr int E = elems_per_thread(H);
   static constexpr int T = H / E;
-  static constexpr int CL0 = (144 * 1024) / ((Row<H, E>::LDS | 1) * 4);
+  static constexpr bool HALF = H >= 512 && H <= 2048;  // two workgroups per CU
+  static constexpr int CL0 = ((HALF ? 72 : 144) * 1024) / ((Row<H, E>::LDS | 1) * 4);
   static constexpr int CL = CL0 >= 64 ? 64 : CL0 >= 32 ? 32 : CL0 >= 16 ? 16 : CL0 >= 8 ? 8 : 4;
   static constexpr int CS = col_stride(Row<H, E>::LDS, CL);
-  static constexpr int CP = cmin(CL, 1024 / T);
+  static constexpr int CP = cmin(CL, (HALF ? 512 : 1024) / T);
   static constexpr int NT = CP * T;
   static constexpr int NP = CL / CP;
   static constexpr int64_t lds_bytes() { return static_cast<int64_t>(CL) * CS * 4; }

@@ -20,6 +20,11 @@ weight rows, one more parameter-sized buffer: a training step's forward
 backward (``circulant_bwd_spec``) reads them instead of transforming the
 weights again; without grad, the spectra are kept across calls until c
 changes, and the forward (``circulant_fwd_spec``) transforms no weight rows.
+
+With ``deterministic=True`` the backward computes dc with ``circulant_bwd_det``:
+each token range's partial sums go to a workspace (allocated through torch,
+one q k p slice per range) and are summed in a fixed order, so c's gradient
+is bitwise the same from run to run.
 """
 
 from __future__ import annotations
@@ -31,6 +36,7 @@ import torch
 from .binding import (
     circulant_bwd,
     circulant_bwd_acc,
+    circulant_bwd_det,
     circulant_bwd_spec,
     circulant_fwd,
     circulant_fwd_spec,
@@ -49,16 +55,21 @@ class BlockCirculantFunction(torch.autograd.Function):
     so the forward clears a gradient buffer in its launch.  Grad mode is off
     inside ``forward``, hence the caller decides.  ``spectra``: the forward
     also writes the weight spectra, which the backward reads.
+    ``deterministic``: dc from ``circulant_bwd_det`` (no gradient buffer, no
+    spectra).
     """
 
     @staticmethod
     def forward(ctx, x: torch.Tensor, c: torch.Tensor, grad_buffer: bool = False,
-                spectra: bool = False) -> torch.Tensor:
+                spectra: bool = False, deterministic: bool = False) -> torch.Tensor:
         x = x.contiguous()
         c = c.contiguous()
         ctx.save_for_backward(x, c)
         ctx.dc = None
         ctx.cs = None
+        ctx.det = deterministic
+        if deterministic:
+            return circulant_fwd(x, c)
         want_dc = grad_buffer and ctx.needs_input_grad[1]
         if want_dc:
             ctx.dc = torch.empty_like(c)  # cleared by the forward launch, filled by the backward
@@ -74,20 +85,21 @@ class BlockCirculantFunction(torch.autograd.Function):
         x, c = ctx.saved_tensors
         need_dx, need_dc = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if not (need_dx or need_dc):
-            return None, None, None, None
+            return None, None, None, None, None
         dc, ctx.dc = ctx.dc, None  # zeroed buffer: good for one backward only
         dy = dy.contiguous()
-        if ctx.cs is not None:
+        if ctx.det and need_dc:
+            dx, dc = circulant_bwd_det(x, c, dy, need_dx=need_dx)
+        elif ctx.cs is not None:
             if need_dc and dc is not None:
                 dx, dc = circulant_bwd_spec(x, ctx.cs, dy, dc=dc, need_dx=need_dx, accumulate=True)
             else:
                 dx, dc = circulant_bwd_spec(x, ctx.cs, dy, need_dx=need_dx, need_dc=need_dc)
-            return dx, dc, None, None
-        if need_dc and dc is not None:
+        elif need_dc and dc is not None:
             dx, dc = circulant_bwd_acc(x, c, dy, dc, need_dx=need_dx)
-            return dx, dc, None, None
-        dx, dc = circulant_bwd(x, c, dy, need_dx=need_dx, need_dc=need_dc)
-        return dx, dc, None, None
+        else:  # dx alone has no token sum, so it is the same in every mode
+            dx, dc = circulant_bwd(x, c, dy, need_dx=need_dx, need_dc=need_dc)
+        return dx, dc, None, None, None
 
 
 class BlockCirculantLinear(torch.nn.Module):
@@ -97,16 +109,20 @@ class BlockCirculantLinear(torch.nn.Module):
     Activations may be float32 or bfloat16 and must live on a GPU.  ``c`` is
     initialised N(0, 1/d_in), the variance that keeps y at the scale of x.
     ``weight_spectra``: keep the packed spectra of the weight rows in one more
-    buffer of c's size (see the module docstring).
+    buffer of c's size; ``deterministic``: a bitwise reproducible gradient of c
+    (see the module docstring; the two do not combine).
     """
 
     def __init__(self, d_in: int, d_out: int, p: int, device=None, generator: torch.Generator | None = None,
-                 weight_spectra: bool = False):
+                 weight_spectra: bool = False, deterministic: bool = False):
         super().__init__()
         if p < 2 or p & (p - 1) or d_in % p or d_out % p:
             raise ValueError("p must be a power of two >= 2 dividing d_in and d_out")
+        if weight_spectra and deterministic:
+            raise ValueError("weight_spectra and deterministic do not combine")
         self.d_in, self.d_out, self.p = d_in, d_out, p
         self.weight_spectra = weight_spectra
+        self.deterministic = deterministic
         c = torch.empty(d_out // p, d_in // p, p, dtype=torch.float32, device=device)
         with torch.no_grad():
             c.normal_(0.0, 1.0 / math.sqrt(d_in), generator=generator)
@@ -124,7 +140,8 @@ class BlockCirculantLinear(torch.nn.Module):
             return circulant_fwd_spec(x.contiguous(), self._cs)
         self._cs = None
         return BlockCirculantFunction.apply(x, self.c, torch.is_grad_enabled() and self.c.requires_grad,
-                                            self.weight_spectra)
+                                            self.weight_spectra, self.deterministic)
 
     def extra_repr(self) -> str:
-        return f"d_in={self.d_in}, d_out={self.d_out}, p={self.p}, weight_spectra={self.weight_spectra}"
+        return (f"d_in={self.d_in}, d_out={self.d_out}, p={self.p}, weight_spectra={self.weight_spectra}, "
+                f"deterministic={self.deterministic}")

@@ -91,6 +91,11 @@ def test_validation(L, fn, args, want):
         assert f(*cargs, None) == STATUS[want]
 
 
+def test_layer_options_that_do_not_combine():
+    with pytest.raises(ValueError):
+        bcl.BlockCirculantLinear(64, 64, 16, device="cpu", weight_spectra=True, deterministic=True)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 

@@ -17,9 +17,10 @@ from tests.gpu_util import TOL, TORCH_DT, device_input, row_relerr, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _layer_with(c: torch.Tensor, weight_spectra: bool = False) -> bcl.BlockCirculantLinear:
+def _layer_with(c: torch.Tensor, weight_spectra: bool = False, deterministic: bool = False) -> bcl.BlockCirculantLinear:
     q, k, p = c.shape
-    layer = bcl.BlockCirculantLinear(k * p, q * p, p, device="cuda:0", weight_spectra=weight_spectra)
+    layer = bcl.BlockCirculantLinear(k * p, q * p, p, device="cuda:0", weight_spectra=weight_spectra,
+                                     deterministic=deterministic)
     with torch.no_grad():
         layer.c.copy_(c)
     return layer
@@ -126,6 +127,31 @@ def test_weight_spectra_steps_and_kept_spectra():
     yo = co.circulant_forward_fft(xr, cr)
     assert torch.equal(y1, y2)
     assert row_relerr(to_f64(y1), yo) <= TOL["bf16"] and row_relerr(to_f64(y3), 2 * yo) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("batch,d,p,dtype", [(256, 4096, 128, "bf16"), (2048, 4096, 1024, "bf16"), (33, 512, 16, "f32")])
+def test_deterministic_layer(batch, d, p, dtype):
+    # deterministic=True: c.grad is bitwise the same over five steps and
+    # matches the oracle; x.grad (no token sum) is the default layer's bit for bit
+    print(f"deterministic layer B={batch} D={d} p={p} {dtype}", flush=True)
+    x, xr = device_input((batch, d), syn.WL_TEST, syn.T_X, 16, dtype=dtype)
+    c, cr = device_input((d // p, d // p, p), syn.WL_TEST, syn.T_C, 16, scale=1 / d**0.5)
+    dy, dyr = device_input((batch, d), syn.WL_TEST, syn.T_DY, 16, dtype=dtype)
+    layer, ref = _layer_with(c, deterministic=True), _layer_with(c)
+    runs = []
+    for _ in range(5):
+        layer.c.grad = None
+        xg = x.detach().clone().requires_grad_(True)
+        layer(xg).backward(dy)
+        runs.append((layer.c.grad.clone(), xg.grad.clone()))
+    xg = x.detach().clone().requires_grad_(True)
+    ref(xg).backward(dy)
+    torch.cuda.synchronize()
+    for gc, gx in runs:
+        assert torch.equal(gc, runs[0][0]) and torch.equal(gx, xg.grad)
+    dxo, dco = co.circulant_backward_fft(xr, cr, dyr)
+    assert row_relerr(to_f64(runs[0][0]).reshape(-1, p), dco.reshape(-1, p)) <= TOL["f32"]
+    assert row_relerr(to_f64(runs[0][1]), dxo) <= TOL[dtype]
 
 
 def test_token_axes_and_transposed_input():

@@ -707,6 +707,107 @@ def profile_circulant(reps=3):
             "spectra")
 
 
+def profile_api():
+    """Every entry point of the library, on buffers allocated beforehand, once
+    to warm up and once more between two of torch's spin kernels, for a HIP API
+    trace (api_summary): the HIP calls on this thread between the two spin
+    launches are the library's and the binding's alone."""
+    a = syn.torch_normal((4096, 512), syn.WL_RDFFT_512, syn.T_X, 0)
+    a2d = syn.torch_normal((1, 1024, 1024), syn.WL_RDFFT_LARGE, syn.T_X, 1)
+    spec = torch.empty(4096, 257, 2, device=a.device)
+    batch, d, p = 256, 4096, 128
+    x = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_X, 0, dtype=torch.bfloat16)
+    dy = syn.torch_normal((batch, d), syn.WL_CIRC_LAYER, syn.T_DY, 0, dtype=torch.bfloat16)
+    c = syn.torch_normal((d // p, d // p, p), syn.WL_CIRC_LAYER, syn.T_C, p, scale=1 / 64.0)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dc, cs = torch.empty_like(c), torch.empty_like(c)
+    ws = torch.empty(bcl.circulant_bwd_det_workspace(batch, d, d, p, True) // 4, device=a.device)
+
+    def calls():
+        bcl.rdfft_forward(a)
+        bcl.rdfft_inverse(a)
+        bcl.rdfft2d_forward(a2d)
+        bcl.rdfft2d_inverse(a2d)
+        bcl.rdfft_unpack(a, spec)
+        bcl.rdfft_pack(spec, a)
+        bcl.circulant_fwd(x, c, y)
+        bcl.circulant_bwd(x, c, dy, dx, dc)
+        bcl.circulant_fwd_zero(x, c, dc, y)
+        bcl.circulant_bwd_acc(x, c, dy, dc, dx)
+        bcl.circulant_bwd_det_workspace(batch, d, d, p, True)
+        bcl.circulant_bwd_det(x, c, dy, dx, dc, ws)
+        bcl.circulant_bwd_det_noalloc(x, c, dy, dx, dc)
+        bcl.circulant_weight_spectra(c, cs)
+        bcl.circulant_fwd_step(x, c, cs, y, dc=dc)
+        bcl.circulant_fwd_spec(x, cs, y, dc=dc)
+        bcl.circulant_bwd_spec(x, cs, dy, dx, dc, accumulate=True)
+
+    calls()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(1000)
+    calls()
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    log("profiled the HIP API calls of every entry point (second pass between two spin kernels)")
+
+
+API_ALLOC = re.compile(r"Malloc|Free|Memset|HostRegister|MemPool|MemAlloc|MemCreate|MemMap")
+
+
+def api_summary(root: str) -> str:
+    """Markdown summary of a rocprofv3 --hip-trace --kernel-trace run of
+    --profile-api (csv under ``root``): the HIP API calls the calling thread
+    made between the launches of the two spin kernels, by function, with the
+    allocation and memset calls among them counted separately."""
+    import csv
+    import glob
+
+    api = glob.glob(os.path.join(root, "**", "*hip_api_trace.csv"), recursive=True)
+    ker = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if not api or not ker:
+        raise SystemExit(f"no hip_api_trace.csv / kernel_trace.csv under {root}")
+    kernels = {r["Correlation_Id"]: r["Kernel_Name"] for r in csv.DictReader(open(ker[0]))}
+    calls = sorted(csv.DictReader(open(api[0])), key=lambda r: int(r["Start_Timestamp"]))
+    spins = [r for r in calls if "spin_kernel" in kernels.get(r["Correlation_Id"], "")]
+    if len(spins) < 2:
+        raise SystemExit("the trace holds fewer than two spin-kernel launches")
+    a, b = spins[-2], spins[-1]
+    t0, t1, tid = int(a["Start_Timestamp"]), int(b["Start_Timestamp"]), a["Thread_Id"]
+    inside = [r for r in calls if r["Thread_Id"] == tid and t0 < int(r["Start_Timestamp"]) < t1]
+    count = {}
+    for r in inside:
+        count[r["Function"]] = count.get(r["Function"], 0) + 1
+    launches = [kernels[r["Correlation_Id"]] for r in inside if r["Correlation_Id"] in kernels]
+    ours = sum(1 for k in launches if "rdfft::" in k)
+    alloc = {f: n for f, n in count.items() if API_ALLOC.search(f)}
+    rows = [f"| `{f}` | {n} |" for f, n in sorted(count.items(), key=lambda kv: (-kv[1], kv[0]))]
+    return "\n".join([
+        "# HIP API calls inside the library's entry points (rocprofv3 HIP trace)",
+        "",
+        "Command (repository root, one MI355X):",
+        "",
+        "```",
+        "rocprofv3 --hip-trace --kernel-trace -d gpurun_out/api -o api --output-format csv -- python3 -u bench.py "
+        "--profile-api",
+        "python3 bench.py --api-summary gpurun_out/api",
+        "```",
+        "",
+        "`--profile-api` calls every entry point (transforms, 2D, pack and unpack, every circulant call,",
+        "the deterministic and allocation-free backwards, the weight-spectra calls) on buffers allocated",
+        "beforehand: once to warm up, then once more between the launches of two of torch's spin kernels.",
+        "Below: every HIP API call the calling thread made between those two launches, that is, the calls",
+        "of the library and of its ctypes binding during the second pass.",
+        "",
+        f"Kernel launches in the window: {len(launches)}, of which {ours} of this library.",
+        f"Allocation, free or memset calls in the window: {sum(alloc.values())}"
+        + (f" ({', '.join(f'{f}: {n}' for f, n in alloc.items())})" if alloc else "") + ".",
+        "",
+        "| HIP function | calls |",
+        "|---|---|",
+        *rows,
+    ]) + "\n"
+
+
 def profile_2d(reps=3):
     """Eager 2D forward and inverse of one 4096x4096 fp32 array, for counter
     collection under a profiler: no graphs, no timing."""
@@ -1015,6 +1116,12 @@ def main():
                     help="first run one plain 256 MiB device copy (a known-size reference for HBM counters)")
     ap.add_argument("--profile-circulant", action="store_true",
                     help="only launch the circulant workloads eagerly, for counter collection, and exit")
+    ap.add_argument("--profile-api", action="store_true",
+                    help="only call every entry point twice (the second time between two spin kernels), for a "
+                         "HIP API trace, and exit")
+    ap.add_argument("--api-summary", metavar="ROOT",
+                    help="write profiles/hip_api_library_calls.md from a HIP API trace of --profile-api under ROOT "
+                         "and exit (no GPU needed)")
     ap.add_argument("--profile-2d", action="store_true",
                     help="only run the 2D forward and inverse of one 4096x4096 fp32 array eagerly, three times, for "
                          "counter collection, and exit")
@@ -1033,6 +1140,9 @@ def main():
         open(os.path.join(PROFILES, "traffic.md"), "w").write(tr)
         if circ:
             open(os.path.join(PROFILES, "traffic_circulant_d4096.md"), "w").write(circ)
+        return
+    if args.api_summary:
+        open(os.path.join(PROFILES, "hip_api_library_calls.md"), "w").write(api_summary(args.api_summary))
         return
     if args.sq_summary:
         open(os.path.join(PROFILES, "counters_circulant_and_transforms.md"), "w").write(
@@ -1067,6 +1177,9 @@ def main():
         return
     if args.profile_2d:
         profile_2d()
+        return
+    if args.profile_api:
+        profile_api()
         return
 
     rows, p, dt = args.rows, args.p, args.dtype

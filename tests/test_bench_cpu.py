@@ -4,8 +4,8 @@ The torch.fft forms that bench.py times beside the layer as context must be
 the same linear map as the block-circulant layer (Paper-Notes, "循环矩阵训练
 适配"): checked here against the oracle's dense forward and backward in float64.
 Also: the algorithmic byte and flop counts of the layer workloads, the split of
-the timed steps into runs (exactly the requested count), and the exit of a
-multi-GPU request.
+the timed steps into runs (exactly the requested count), the exit of a
+multi-GPU request, and the window and allocation count of the HIP API summary.
 """
 import os
 
@@ -68,3 +68,26 @@ def test_more_than_one_gpu_exits_with_a_message():
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_api_summary_window_and_allocation_count(tmp_path):
+    # a fabricated trace: two spin-kernel launches on thread 1, and between
+    # them one library launch, a hipMalloc on thread 1 and a hipFree on thread
+    # 2 (another thread: outside the window); a hipMalloc before the first spin
+    api = [("hipMalloc", 1, 5, 10), ("hipLaunchKernel", 1, 1, 20), ("hipLaunchKernel", 1, 2, 30),
+           ("hipMalloc", 1, 6, 35), ("hipFree", 2, 7, 36), ("hipGetLastError", 1, 8, 37),
+           ("hipLaunchKernel", 1, 3, 40)]
+    ker = {1: "at::cuda::(anonymous namespace)::spin_kernel(long)", 2: "void rdfft::rdfft_fwd_kernel<512>()",
+           3: "at::cuda::(anonymous namespace)::spin_kernel(long)"}
+    with open(tmp_path / "api_hip_api_trace.csv", "w") as f:
+        f.write("Domain,Function,Process_Id,Thread_Id,Correlation_Id,Start_Timestamp,End_Timestamp\n")
+        for fn, tid, cid, t in api:
+            f.write(f"HIP_RUNTIME_API,{fn},9,{tid},{cid},{t},{t + 1}\n")
+    with open(tmp_path / "api_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Correlation_Id,Start_Timestamp,End_Timestamp\n")
+        for cid, name in ker.items():
+            f.write(f"\"{name}\",{cid},{100 + cid},{110 + cid}\n")
+    md = bench.api_summary(str(tmp_path))
+    assert "Kernel launches in the window: 1, of which 1 of this library." in md
+    assert "Allocation, free or memset calls in the window: 1 (hipMalloc: 1)." in md
+    assert "| `hipGetLastError` | 1 |" in md and "hipFree" not in md.split("| HIP function")[1]

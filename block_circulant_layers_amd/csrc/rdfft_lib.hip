@@ -185,14 +185,48 @@ int64_t tokens_per_wg(int64_t batch, int64_t tiles, int tb, int64_t target = kTa
   return (tpw + tb - 1) / tb * tb;
 }
 
+// one-block layers (d_in = d_out = p) on circ_one_kernel, with the side jobs
+// of the token-persistent kernel (clear zero[0..nzero); forward from c: store
+// the weight spectrum into wout)
+template <int P, class Io, bool WSPEC>
+int launch_circ_one(const void* in, const float* c, void* out, int64_t batch, bool trans, hipStream_t s, float* zero,
+                    int64_t nzero, bool* zeroed, float* wout, bool* wout_done) {
+  constexpr int NT = P / elems_per_thread(P);
+  const int64_t cap = static_cast<int64_t>(device_cus()) * kOneWgPerCu;
+  const int64_t grid = batch < 1 ? 1 : batch < cap ? batch : cap;
+  if (!zero) nzero = 0;
+  const bool wo = wout != nullptr && !trans && !WSPEC && batch > 0;
+  const auto* pi = static_cast<const typename Io::T*>(in);
+  auto* po = static_cast<typename Io::T*>(out);
+  if (trans)
+    hipLaunchKernelGGL((circ_one_kernel<P, true, Io, WSPEC>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, pi, c,
+                       po, batch, zero, nzero, static_cast<float*>(nullptr));
+  else
+    hipLaunchKernelGGL((circ_one_kernel<P, false, Io, WSPEC>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, pi,
+                       c, po, batch, zero, nzero, wo ? wout : nullptr);
+  if (zeroed) *zeroed = nzero > 0;
+  if (wout_done) *wout_done = wo;
+  return launch_status();
+}
+
+// row lengths whose one-block layers take circ_one_kernel
+template <int P>
+constexpr bool one_block_kernel() {
+  return P == 4096;
+}
+
 // y = circulant product of `in` (forward, or transposed for dx).  When the
-// token-persistent kernel runs, it also clears zero[0..nzero) and sets
-// *zeroed, and (forward from c) stores the weight spectra into wout if given;
-// otherwise zero and wout are left alone.
+// token-persistent kernel (or the one-block kernel) runs, it also clears
+// zero[0..nzero) and sets *zeroed, and (forward from c) stores the weight
+// spectra into wout if given; otherwise zero and wout are left alone.
 template <int P, class Io, bool WSPEC = false>
 int launch_circ_product(const void* in, const float* c, void* out, int64_t batch, int64_t nin, int64_t nout, bool trans,
                         hipStream_t s, float* zero = nullptr, int64_t nzero = 0, bool* zeroed = nullptr,
                         float* wout = nullptr, bool* wout_done = nullptr) {
+  if constexpr (one_block_kernel<P>()) {
+    if (nin == 1 && nout == 1)
+      return launch_circ_one<P, Io, WSPEC>(in, c, out, batch, trans, s, zero, nzero, zeroed, wout, wout_done);
+  }
   if constexpr (P >= 64) {
     using S = TpShape<P, false, WSPEC>;
     if (nin <= S::CR && S::fits(static_cast<int>(nin)) && S::lds_bytes(static_cast<int>(nin)) <= kMaxLds &&

@@ -92,6 +92,18 @@ def test_workload_adapter_shape(adapter, step):
          step=step)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("batch", [1, 2, 3, 257, 1100])
+@pytest.mark.parametrize("step", [False, True])
+def test_one_block_layers(batch, dtype, step):
+    """d_in = d_out = p = 4096, a layer of one circulant block: the forward
+    takes its own kernel (the product on the forward's last-pass registers),
+    the backward with dx and dc the one-launch kernel of every p.  Batches
+    leave workgroups without a token (1, 3), end in a ragged round (257) or
+    make every workgroup loop over several tokens (1100)."""
+    _run(batch, 4096, 4096, 4096, dtype, index=batch, c_scale=1 / 64.0, dense=False, step=step)
+
+
 def test_adjoint_identities_on_gpu_outputs():
     (x, c, dy, y, dx, dc), _ = _run(512, 4096, 4096, 1024, "f32", index=5, c_scale=1 / 64.0, dense=False)
     s1 = float((dy.double() * y.double()).sum())

@@ -1046,12 +1046,14 @@ def counter_summary(root: str):
         for name, batch, pp in (("adapter", 2048, 1024), ("D=4096 B=256 p=128", 256, 128),
                                 ("D=4096 B=256 p=512", 256, 512), ("D=4096 B=256 p=4096", 256, 4096)):
             act, cb = batch * 4096 * 2, 4096 * 4096 // pp * 4
+            # a layer of one block (d = p) runs its forward on circ_one_kernel
+            fwd = "circ_one_kernel" if pp == 4096 else "circ_tp_kernel"
             work += [
-                (f"circ_tp_kernel<{pp}, false, rdfft::Bf16Io, false>", f"{name} forward", kib(act + cb),
+                (f"{fwd}<{pp}, false, rdfft::Bf16Io, false>", f"{name} forward", kib(act + cb),
                  kib(act + cb)),
                 (f"circ_bwd_kernel<{pp}, rdfft::Bf16Io, false, false>", f"{name} backward (dx and dc)",
                  kib(2 * act + cb), kib(act + cb)),
-                (f"circ_tp_kernel<{pp}, false, rdfft::Bf16Io, true>", f"{name} forward from the weight spectra",
+                (f"{fwd}<{pp}, false, rdfft::Bf16Io, true>", f"{name} forward from the weight spectra",
                  kib(act + cb), kib(act)),
                 (f"circ_bwd_kernel<{pp}, rdfft::Bf16Io, false, true>",
                  f"{name} backward from the weight spectra (dx and dc)", kib(2 * act + cb), kib(act + cb)),

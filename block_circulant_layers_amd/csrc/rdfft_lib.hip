@@ -307,7 +307,11 @@ int launch_circ_dc_any(const void* x, const void* dy, float* dc, int64_t batch, 
 
 // dx and dc in one launch (circ_bwd_kernel) where the row length allows it and
 // the dx tiles fit; returns false when the caller must take the two-kernel path.
-constexpr int64_t kBwdDxWgs = 256;  // dx workgroups the fused token split aims at
+// dx workgroups the fused token split aims at: 128 beside the 128 dc
+// workgroups fill the chip in one round of workgroups (D=4096 B=256 bf16
+// training step, 256 -> 128: p=128 5.24 -> 5.61 M tokens/s, p=512 7.59 ->
+// 8.58 M, p=4096 and the adapter shape unchanged; 64 and 96 slower everywhere)
+constexpr int64_t kBwdDxWgs = 128;
 
 // whether dx and dc of this shape run in one launch (circ_bwd_kernel)
 template <int P, bool WSPEC = false>

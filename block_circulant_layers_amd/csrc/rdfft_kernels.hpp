@@ -15,11 +15,14 @@ namespace rdfft {
 // elements per thread for row length P
 __host__ __device__ constexpr int elems_per_thread(int P) { return P < 16 ? P : 16; }
 // threads per workgroup of the standalone kernels: one wavefront for rows of
-// p <= 512 (workgroups of one wave run their passes without waiting for
-// other waves: 4096x512 fp32 forward 4.86 -> 4.46 us against 256 threads),
+// p <= 1024 (workgroups of one wave run their passes without waiting for
+// other waves: 4096x512 fp32 forward 4.86 -> 4.46 us against 256 threads;
+// at p = 1024, one row a workgroup against four: 4096x1024 fp32 forward +
+// inverse 52.1-52.6% -> 55.2-56.1% of HBM over three runs, 16384x1024 +1
+// point, bf16 +2%; at p = 2048 one row of 128 threads measured slower),
 // else at least 256, or one whole row
 __host__ __device__ constexpr int wg_threads(int P, int E) {
-  return (P / E) > (P <= 512 ? 64 : 256) ? (P / E) : (P <= 512 ? 64 : 256);
+  return (P / E) > (P <= 1024 ? 64 : 256) ? (P / E) : (P <= 1024 ? 64 : 256);
 }
 // elements per thread of the standalone kernels (32, with one exchange fewer,
 // measured slower: 4096x512 fp32 forward 7.2 us against 4.9 us, and 31.3
@@ -30,11 +33,14 @@ __host__ __device__ constexpr int standalone_elems(int P, bool /*f32*/) { return
 // faster than four; a second group of look-ahead measured slower; the fp32
 // forward at p = 2048 and 4096 takes three (4096x2048 16.5 -> 14.5 us,
 // 4096x4096 27.8 -> 26.5 us), while three slowed the inverse there and both
-// directions at p = 1024; 16-bit rows of 1024 <= p <= 4096: four; p = 8192
-// (512 threads): two, as four would cap registers at 64 and spill; p <= 512:
-// eight one-wave workgroups)
+// directions at p = 1024 with 256-thread workgroups; 16-bit rows of
+// 2048 <= p <= 4096: four; p = 8192 (512 threads): two, as four would cap
+// registers at 64 and spill; p <= 512: eight one-wave workgroups; p = 1024:
+// eight one-wave workgroups for fp32, sixteen for 16-bit rows)
 __host__ __device__ constexpr int wg_per_cu(int P, bool f32, bool inv) {
-  return P >= 1024 ? (f32 || P >= 8192 ? ((!inv && f32 && (P == 2048 || P == 4096)) ? 3 : 2) : 4) : 8;
+  return P == 1024 ? (f32 ? 8 : 16)
+         : P > 1024 ? (f32 || P >= 8192 ? ((!inv && f32 && (P == 2048 || P == 4096)) ? 3 : 2) : 4)
+                    : 8;
 }
 // Forward kernels that stage the transformed row in LDS and store it in the
 // aligned element order t + T*s, instead of storing the last pass's packed

@@ -32,14 +32,16 @@ __host__ __device__ constexpr int standalone_elems(int P, bool /*f32*/) { return
 // rows of p >= 1024: two workgroups, each looping over more groups, measured
 // faster than four; a second group of look-ahead measured slower; the fp32
 // forward at p = 2048 and 4096 takes three (4096x2048 16.5 -> 14.5 us,
-// 4096x4096 27.8 -> 26.5 us), while three slowed the inverse there and both
-// directions at p = 1024 with 256-thread workgroups; 16-bit rows of
+// 4096x4096 27.8 -> 26.5 us), and so does the inverse at p = 2048 (4096x2048
+// 14.3 -> 13.7 us over three runs), while three slowed the inverse at p = 4096
+// (25.4 -> 25.7 us) and four the forward at p = 2048 (14.3 -> 15.5 us), and
+// three slowed both directions at p = 1024 with 256-thread workgroups; 16-bit rows of
 // 2048 <= p <= 4096: four; p = 8192 (512 threads): two, as four would cap
 // registers at 64 and spill; p <= 512: eight one-wave workgroups; p = 1024:
 // eight one-wave workgroups for fp32, sixteen for 16-bit rows)
 __host__ __device__ constexpr int wg_per_cu(int P, bool f32, bool inv) {
   return P == 1024 ? (f32 ? 8 : 16)
-         : P > 1024 ? (f32 || P >= 8192 ? ((!inv && f32 && (P == 2048 || P == 4096)) ? 3 : 2) : 4)
+         : P > 1024 ? (f32 || P >= 8192 ? ((f32 && (P == 2048 || (!inv && P == 4096))) ? 3 : 2) : 4)
                     : 8;
 }
 // Forward kernels that stage the transformed row in LDS and store it in the

@@ -1330,7 +1330,7 @@ def main():
         extra["rdfft2d_4096x4096_f32"] = bench_rdfft2d(4096, 4096, 256, 32)
         log("extra: unpack / pack 4096x512 f32")
         extra["spectrum_unpack_pack_4096x512_f32"] = bench_spectrum(4096, 512, 1024, 128)
-        for mib in (8, 16, 32, 64):
+        for mib in (4, 8, 16, 32, 64):
             if mib in (8, 64):
                 log(f"extra: device copy {mib} MiB")
                 extra[f"copy_ceiling_{mib}mib"] = bench_copy(mib << 20, 1024, 128)
